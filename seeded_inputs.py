@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and bench.py.
+
+This module holds no attention arithmetic: it only draws i.i.d. standard-normal
+tensors from a seeded PCG64 generator and quantises them to bfloat16 with
+round-to-nearest-even on the integer bit pattern.  The GPU receives exactly the
+bf16 bits produced here; the oracle receives the same values upcast to float64.
+
+Workloads (the five problem sizes of the FlashAttention-2 backward study):
+  c1  B=1 H=1  N=48    d=16  fp32  non-causal and causal, oracle O/L
+  c2  B=1 H=8  N=1024  d=64  bf16  non-causal
+  c3  B=1 H=32 N=8192  d=128 bf16  non-causal and causal
+  c4  B=4 H=16 N=4000  d=128 bf16  causal, Q multiplied by 4 after drawing
+  c5  B=1 H=8  N=32768 d=128 bf16  causal
+Q, K, V, dO are drawn in that order from one generator per workload with
+seed c1=0 .. c5=4; the scale is 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "fp32" or "bf16"
+    causal: tuple         # causal modes this workload is run in
+    seed: int
+    q_mult: float = 1.0   # applied to Q after drawing (exact in bf16 for powers of two)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, causal: bool) -> float:
+        """Backward FLOP count 10*B*H*N^2*d, halved under the causal mask."""
+        f = 10.0 * self.B * self.H * self.N * self.N * self.d
+        return 0.5 * f if causal else f
+
+
+WORKLOADS = {
+    "c1": Workload("c1", 1, 1, 48, 16, "fp32", (False, True), 0),
+    "c2": Workload("c2", 1, 8, 1024, 64, "bf16", (False,), 1),
+    "c3": Workload("c3", 1, 32, 8192, 128, "bf16", (False, True), 2),
+    "c4": Workload("c4", 4, 16, 4000, 128, "bf16", (True,), 3, q_mult=4.0),
+    "c5": Workload("c5", 1, 8, 32768, 128, "bf16", (True,), 4),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16 (round-to-nearest-even), returned as uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(x)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass
+class Inputs:
+    """Q, K, V, dO as float32 arrays holding exactly representable values.
+
+    For bf16 workloads ``bits`` holds the uint16 patterns that go to the GPU and
+    the float32 arrays are their exact widening.
+    """
+    wl: Workload
+    Q: np.ndarray
+    K: np.ndarray
+    V: np.ndarray
+    dO: np.ndarray
+    bits: dict = field(default_factory=dict)
+
+
+def draw(wl: Workload, *, B=None, H=None, N=None, d=None, seed=None, q_mult=None,
+         dtype=None) -> Inputs:
+    """Draw Q, K, V, dO of shape [B,H,N,d] for a workload (fields overridable)."""
+    B = wl.B if B is None else B
+    H = wl.H if H is None else H
+    N = wl.N if N is None else N
+    d = wl.d if d is None else d
+    seed = wl.seed if seed is None else seed
+    q_mult = wl.q_mult if q_mult is None else q_mult
+    dtype = wl.dtype if dtype is None else dtype
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (B, H, N, d)
+    arrs = [rng.standard_normal(shape, dtype=np.float32) for _ in range(4)]
+    if q_mult != 1.0:
+        arrs[0] = arrs[0] * np.float32(q_mult)
+    names = ("Q", "K", "V", "dO")
+    wl2 = Workload(wl.name, B, H, N, d, dtype, wl.causal, seed, q_mult)
+    if dtype == "bf16":
+        bits = {n: f32_to_bf16_bits(a) for n, a in zip(names, arrs)}
+        vals = [bf16_bits_to_f32(bits[n]) for n in names]
+        return Inputs(wl2, *vals, bits=bits)
+    if dtype == "fp32":
+        return Inputs(wl2, *arrs)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def draw_custom(B, H, N, d, dtype, seed, q_mult=1.0) -> Inputs:
+    """Draw inputs for an arbitrary shape (edge-case tests)."""
+    wl = Workload("custom", B, H, N, d, dtype, (False, True), seed, q_mult)
+    return draw(wl)
