@@ -1,0 +1,24 @@
+// launch.hpp -- internal launcher interface between the C ABI (api.hip) and the
+// kernel translation units.  Each launcher assumes validated arguments and
+// returns the hipError_t of its launch.
+#pragma once
+
+#include "common.hpp"
+
+namespace fa {
+
+hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D,
+                             float* dq_accum, Shape s, hipStream_t st);
+
+hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s,
+                             float scale, hipStream_t st);
+
+hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, void* O,
+                      float* L, Shape s, float scale, bool causal, hipStream_t st);
+
+hipError_t launch_bwd(int dtype, const void* Q, const void* K, const void* V,
+                      const void* dO, const float* L, const float* D, float* dq_accum,
+                      void* dK, void* dV, Shape s, float scale, bool causal,
+                      hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention-2 backward on one MI355X.
+
+A step is one pass of the whole backward hot path -- fa_bwd_preprocess (D and
+dq_accum := 0), fa_bwd (main kernel) and fa_bwd_convert_dq -- over one batch
+of synthetic inputs already resident in HBM.  The forward that produces O and
+L runs once before timing and is not timed.
+
+Workload (default): B=1, H=32, N=8192, d=128, bf16, non-causal; the causal
+variant of the same shape is timed too and reported under "causal".
+FLOPs per step: 10*B*H*N^2*d, halved under the causal mask.
+
+Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention backward TFLOP/s (10·B·H·N²·d, halved causal) and % bf16 MFMA peak"
+MAIN_KERNEL_SOURCES = ["attention_fa_bwd_amd/csrc/bwd_simt.hip", "attention_fa_bwd_amd/csrc/bwd_mfma.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_main_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--causal", action="store_true", help="primary line is the causal run")
+    p.add_argument("--no-extra", action="store_true", help="skip the second causal mode")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain 512 MiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in MAIN_KERNEL_SOURCES + ["attention_fa_bwd_amd/csrc/common.hpp"]:
+        path = os.path.join(ROOT, rel)
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, causal: bool):
+    """HBM bytes per main-kernel launch from committed rocprofv3 counter runs,
+    or None when they are missing or were taken on other kernel sources."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    key = f"{workload}_{'causal' if causal else 'full'}"
+    ent = rec.get("entries", {}).get(key)
+    if not ent or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    n = 512 * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 5}))
+
+
+def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    q, k, v, do, o, L = inputs
+    B, H, N, d = q.shape
+    scale = wl.scale
+    D = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dqa = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa_bwd_preprocess(o, do, D, dqa, stream)
+        if evs:
+            evs[1].record(stream)
+        fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, scale, causal, stream)
+        if evs:
+            evs[2].record(stream)
+        fa.fa_bwd_convert_dq(dqa, dq, scale, stream)
+        if evs:
+            evs[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: K whole steps; HIP events on the launch stream split it per kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    pre = [e[0].elapsed_time(e[1]) for e in evs]
+    main = [e[1].elapsed_time(e[2]) for e in evs]
+    conv = [e[2].elapsed_time(e[3]) for e in evs]
+    return {
+        "ms_per_step": total_ms / steps,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "main_ms_mean": statistics.fmean(main), "main_ms_min": min(main),
+        "main_ms_median": statistics.median(main),
+        "pre_ms_mean": statistics.fmean(pre), "conv_ms_mean": statistics.fmean(conv),
+    }
+
+
+def cpu_baseline(wl, causal: bool, budget_s: float):
+    """The oracle's full backward (by definition) on a bounded sample of heads."""
+    import numpy as np
+
+    import oracle
+    import seeded_inputs as si
+    cores = oracle.max_threads()
+    sample = si.draw(wl, B=1, H=1)             # same shape per head, same recipe
+    Q, K, V, G = (np.ascontiguousarray(x, dtype=np.float64) for x in (sample.Q, sample.K, sample.V, sample.dO))
+    heads, elapsed = 0, 0.0
+    while elapsed < budget_s and heads < wl.B * wl.H:
+        t0 = time.perf_counter()
+        oracle.attn_bwd(Q, K, V, G, wl.scale, causal)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    flop = 10.0 * wl.N * wl.N * wl.d * (0.5 if causal else 1.0) * heads
+    return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} head(s) of N={wl.N}, d={wl.d} ({'causal' if causal else 'non-causal'}), "
+                      f"fp64 backward by definition, {elapsed:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+              "heads shard across GPUs with no communication, see the design notes.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    import seeded_inputs as si
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    wl = si.WORKLOADS[args.workload]
+    modes = [args.causal] if args.no_extra else [args.causal, not args.causal]
+    modes = [m for m in modes if m in (False, True)]
+    inp = si.draw(wl)
+    up = {n: torch.from_numpy(inp.bits[n].view(np.int16)).view(torch.bfloat16).cuda()
+          for n in ("Q", "K", "V", "dO")}
+    results = {}
+    for causal in modes:
+        o, L = fa.forward(up["Q"], up["K"], up["V"], wl.scale, causal)
+        torch.cuda.synchronize()
+        r = gpu_time(wl, causal, args.steps, args.warmup, (up["Q"], up["K"], up["V"], up["dO"], o, L))
+        flops = wl.flops(causal)
+        r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
+        r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
+        r["main_tflops"] = flops / (r["main_ms_mean"] * 1e-3) / 1e12
+        results[causal] = r
+        del o, L
+    prim = results[args.causal]
+    traffic = load_traffic(args.workload, args.causal)
+    main_achieved = prim["main_tflops"]
+    line = {
+        "metric": METRIC,
+        "value": round(prim["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded standard normal Q, K, V, dO)",
+        "config": {"workload": f"B={wl.B} H={wl.H} N={wl.N} d={wl.d} bf16 "
+                               f"{'causal' if args.causal else 'non-causal'}",
+                   "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": args.causal,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(prim["pct_peak"], 2),
+        "split_ms": {"preprocess": round(prim["pre_ms_mean"], 4), "main": round(prim["main_ms_mean"], 4),
+                     "convert": round(prim["conv_ms_mean"], 4)},
+        "roofline": {"bound": "mfma", "kernel": "fa_bwd main kernel",
+                     "achieved": round(main_achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(main_achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "flop_per_launch": wl.flops(args.causal),
+                     "avg_launch_ms": round(prim["main_ms_mean"], 4)},
+    }
+    if len(results) > 1:
+        other = results[not args.causal]
+        line["causal" if not args.causal else "non_causal"] = {
+            "value": round(other["tflops"], 3), "ms_per_step": round(other["ms_per_step"], 4),
+            "pct_bf16_peak": round(other["pct_peak"], 2),
+            "main_ms": round(other["main_ms_mean"], 4),
+            "main_frac": round(other["main_tflops"] / PEAK_BF16_TFLOPS, 4)}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

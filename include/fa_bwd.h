@@ -1,0 +1,129 @@
+/*
+ * fa_bwd.h -- C ABI of the MI355X (gfx950) FlashAttention-2 backward library
+ * (libfa_bwd.so).
+ *
+ * The method: "CUDA 算子工程：手写 FlashAttention v2 之路", chapter 16 "FA2 反向：
+ * dQ/dK/dV 的重计算".  Given Q, K, V, O, dO and the per-row logsumexp L of the
+ * forward, the backward produces dQ, dK and dV without materialising the N x N
+ * probability matrix: a preprocess computes D = rowsum(O * dO) (sec 16.1 and
+ * sec 16.8 item 1), the main kernel runs key blocks outer and query blocks
+ * inner (sec 16.2), recomputes S = scale * Q K^T and P = exp(S - L) on chip
+ * (sec 16.4), forms dS = P * (dP - D) and accumulates dV = P^T dO, dK = dS^T Q
+ * per key block and dQ = dS K into an fp32 buffer (sec 16.3, the fp32
+ * accumulation-buffer variant), and a convert step scales dQ and casts it
+ * (sec 16.3 and 16.6).
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d] row-major
+ *              (d fastest) in the element type `dtype`.  L, D: contiguous
+ *              [B, H, N] fp32.  dq_accum: contiguous [B, H, N, d] fp32.
+ *   dtype      FA_DTYPE_F32 (IEEE float) or FA_DTYPE_BF16 (bfloat16 bits).
+ *              L, D and dq_accum are always fp32.
+ *   Scores     S_ij = scale * Q_i . K_j; L_i = log sum_j exp(S_ij) over the
+ *              visible keys (natural log).  causal != 0 hides key j from
+ *              query i when j > i (0-based, diagonal kept).
+ *   Pointers   device pointers (hipMalloc'd or equivalent), owned by the
+ *              caller, at least 16-byte aligned.  Outputs must not alias
+ *              inputs.  The library allocates nothing and keeps no mutable
+ *              global state; calls on different streams may run concurrently
+ *              as long as their buffers are disjoint.
+ *   Stream     `stream` is a hipStream_t passed as void*; NULL is the null
+ *              stream.  Every call only enqueues work and returns; the caller
+ *              synchronises.
+ *   Sizes      B, H, N, d >= 1; B * H * N * d < 2^40; B and H < 65536.
+ *              Supported head dims: d in {16, 32, 64, 128} for both dtypes.
+ *   Errors     every call returns an fa_status_t.  Arguments are validated
+ *              before any device work: FA_EINVAL for a NULL pointer, a
+ *              non-positive or oversized dimension or an unknown dtype;
+ *              FA_EUNSUPPORTED for an unsupported head dim.  FA_EHIP when the
+ *              HIP runtime reports an error (no device, launch failure); the
+ *              raw hipError_t is available from fa_last_hip_error().  No call
+ *              aborts or throws.
+ */
+#ifndef FA_BWD_H
+#define FA_BWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_EINVAL = 1,
+    FA_EUNSUPPORTED = 2,
+    FA_EHIP = 3
+} fa_status_t;
+
+/*
+ * fa_fwd_lse -- attention forward producing O and the logsumexp L that the
+ * backward consumes.  Query blocks outer, key blocks inner with the online
+ * softmax (running max m, denominator l, accumulator a rebased by
+ * alpha = exp(m - m') at each key block), O = a / l and L = m + log l
+ * (1point3acres post "手扒了FlashAttention", the online-softmax recurrence and
+ * the logsumexp; FA2 chapter 16 sec 16.4).  Supporting step of the backward:
+ * it provides O and L for benchmarking and end-to-end checks.
+ *   in : Q, K, V [B,H,N,d] dtype
+ *   out: O [B,H,N,d] dtype (rounded to nearest even for bf16), L [B,H,N] fp32
+ */
+int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V,
+               void* O, float* L,
+               int B, int H, int N, int d, float scale, int causal,
+               void* stream);
+
+/*
+ * fa_bwd_preprocess -- D_i = sum_k O_ik dO_ik with fp32 accumulation (FA2
+ * chapter 16 sec 16.1, the identity D_i = dO_i . O_i, and sec 16.8 item 1:
+ * computed once before the main loop), and dq_accum := 0 so that the main
+ * kernel can accumulate into it.
+ *   in : O, dO [B,H,N,d] dtype
+ *   out: D [B,H,N] fp32 (written), dq_accum [B,H,N,d] fp32 (zeroed)
+ */
+int fa_bwd_preprocess(int dtype, const void* O, const void* dO,
+                      float* D, float* dq_accum,
+                      int B, int H, int N, int d, void* stream);
+
+/*
+ * fa_bwd -- the main backward kernel (FA2 chapter 16 sec 16.2 loop order,
+ * sec 16.6 skeleton): one workgroup per (key block, head, batch); per query
+ * block it recomputes S = scale Q K^T and P = exp(S - L), forms
+ * dP = dO V^T and dS = P (dP - D), accumulates dV += P^T dO and
+ * dK += dS^T Q in registers, and adds the unscaled dS K into dq_accum with
+ * fp32 atomics (sec 16.3, the fp32 accumulation-buffer variant).  Under the
+ * causal mask, query blocks wholly above the diagonal are skipped (sec 16.8
+ * item 2).  dK is multiplied by `scale` at write-out (sec 16.6).
+ *   in : Q, K, V, dO [B,H,N,d] dtype; L, D [B,H,N] fp32
+ *   in/out: dq_accum [B,H,N,d] fp32 -- must hold zeros (fa_bwd_preprocess)
+ *           or earlier partial sums; receives += sum_j dS_ij K_j (unscaled)
+ *   out: dK, dV [B,H,N,d] dtype
+ * dK and dV are bitwise reproducible; dq_accum is a sum of atomics whose order
+ * varies from run to run.
+ */
+int fa_bwd(int dtype, const void* Q, const void* K, const void* V,
+           const void* dO, const float* L, const float* D,
+           float* dq_accum, void* dK, void* dV,
+           int B, int H, int N, int d, float scale, int causal,
+           void* stream);
+
+/*
+ * fa_bwd_convert_dq -- dQ = scale * dq_accum cast to dtype (round to nearest
+ * even for bf16) (FA2 chapter 16 sec 16.3: the separate kernel that applies
+ * the softmax scale and converts the fp32 accumulation buffer).
+ *   in : dq_accum [B,H,N,d] fp32
+ *   out: dQ [B,H,N,d] dtype
+ */
+int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ,
+                      int B, int H, int N, int d, float scale, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+/* The hipError_t of the calling thread's most recent FA_EHIP, or 0. */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_BWD_H */

@@ -1,0 +1,99 @@
+"""CPU-only checks of the C ABI boundary: the library loads, exports every
+symbol include/fa_bwd.h declares, and rejects bad arguments before touching a
+device.  Also checks that the oracle and the GPU path share no code."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_fa_bwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load()
+    names = _declared()
+    assert {"fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq",
+            "fa_strerror"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_has_same_names():
+    for n in ("fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq", "fa_strerror"):
+        assert callable(getattr(fa, n))
+
+
+def test_strerror():
+    for code in (0, 1, 2, 3, 99):
+        s = fa.fa_strerror(code)
+        assert isinstance(s, str) and s
+
+
+ALIGNED = 4096   # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def _bwd(lib, **kw):
+    a = dict(dtype=1, ptr=ALIGNED, B=1, H=1, N=8, d=64)
+    a.update(kw)
+    p = a["ptr"]
+    return lib.fa_bwd(a["dtype"], p, p, p, p, p, p, p, p, p, a["B"], a["H"], a["N"], a["d"],
+                      0.125, 0, None)
+
+
+def test_invalid_arguments_rejected_before_device_work():
+    lib = fa.load()
+    assert _bwd(lib, ptr=None) == fa.FA_EINVAL
+    assert _bwd(lib, ptr=ALIGNED + 4) == fa.FA_EINVAL        # misaligned
+    assert _bwd(lib, B=0) == fa.FA_EINVAL
+    assert _bwd(lib, N=-3) == fa.FA_EINVAL
+    assert _bwd(lib, dtype=7) == fa.FA_EINVAL
+    assert _bwd(lib, B=70000) == fa.FA_EINVAL
+    assert _bwd(lib, B=60000, H=60000, N=60000, d=128) == fa.FA_EINVAL   # > 2^40 elements
+    p = ALIGNED
+    assert lib.fa_fwd_lse(1, p, p, None, p, p, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_preprocess(1, p, p, p, None, 1, 1, 8, 64, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_convert_dq(0, None, p, 1, 1, 8, 64, 0.1, None) == fa.FA_EINVAL
+
+
+@pytest.mark.parametrize("d", [8, 48, 96, 256])
+def test_unsupported_head_dim(d):
+    lib = fa.load()
+    p = ALIGNED
+    assert _bwd(lib, d=d) == fa.FA_EUNSUPPORTED
+    assert lib.fa_fwd_lse(0, p, p, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_bwd_preprocess(1, p, p, p, p, 1, 1, 8, d, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_bwd_convert_dq(1, p, p, 1, 1, 8, d, 0.1, None) == fa.FA_EUNSUPPORTED
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x, 0.25, False)
+
+
+def _sources(*dirs, exts=(".py", ".hip", ".hpp", ".h", ".c", ".cpp")):
+    for d in dirs:
+        for base, _, files in os.walk(os.path.join(ROOT, d)):
+            for f in files:
+                if f.endswith(exts):
+                    yield os.path.join(base, f)
+
+
+def test_oracle_and_gpu_path_share_no_code():
+    for f in _sources("oracle"):
+        t = open(f, encoding="utf-8").read()
+        assert "attention_fa_bwd_amd" not in t and "fa_bwd.h" not in t, f
+    for f in _sources("attention_fa_bwd_amd", "include"):
+        t = open(f, encoding="utf-8").read()
+        assert not re.search(r"\boracle\b", t), f
