@@ -68,9 +68,14 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum, dK, dV});
     if (rc != FA_OK) return rc;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_bwd(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV,
-                                     fa::Shape{B, H, N, d}, scale, causal != 0,
-                                     (hipStream_t)stream));
+    const fa::Shape s{B, H, N, d};
+    const hipStream_t st = (hipStream_t)stream;
+    // one kernel per (dtype, head dim): matrix cores for bf16 d=128, vector ALUs otherwise
+    if (dtype == FA_DTYPE_BF16 && d == 128)
+        return hip_status(fa::launch_bwd_mfma_d128(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
+                                                   causal != 0, st));
+    return hip_status(fa::launch_bwd_simt(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
+                                          causal != 0, st));
 }
 
 int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ, int B, int H, int N, int d,

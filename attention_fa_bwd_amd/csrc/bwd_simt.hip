@@ -164,7 +164,7 @@ static hipError_t bwd_d(const void* Q, const void* K, const void* V, const void*
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* V, const void* dO,
                       const float* L, const float* D, float* dq_accum, void* dK, void* dV,
                       Shape s, float scale, bool causal, hipStream_t st) {
     return dtype == DT_BF16
