@@ -71,9 +71,13 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
     const fa::Shape s{B, H, N, d};
     const hipStream_t st = (hipStream_t)stream;
     // one kernel per (dtype, head dim): matrix cores for bf16 d=128, vector ALUs otherwise
-    if (dtype == FA_DTYPE_BF16 && d == 128)
-        return hip_status(fa::launch_bwd_mfma_d128(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
+    if (dtype == FA_DTYPE_BF16 && d == 128) {
+        int rc2 = hip_status(fa::launch_bwd_dq_d128(Q, K, V, dO, L, D, dq_accum, s, scale,
+                                                    causal != 0, st));
+        if (rc2 != FA_OK) return rc2;
+        return hip_status(fa::launch_bwd_dkdv_d128(Q, K, V, dO, L, D, dK, dV, s, scale,
                                                    causal != 0, st));
+    }
     return hip_status(fa::launch_bwd_simt(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
                                           causal != 0, st));
 }

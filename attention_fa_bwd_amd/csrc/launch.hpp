@@ -22,9 +22,13 @@ hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* 
                            void* dK, void* dV, Shape s, float scale, bool causal,
                            hipStream_t st);
 
-// Matrix-core backward: bf16, head dim 128.
-hipError_t launch_bwd_mfma_d128(const void* Q, const void* K, const void* V, const void* dO,
-                                const float* L, const float* D, float* dq_accum, void* dK,
-                                void* dV, Shape s, float scale, bool causal, hipStream_t st);
+// Matrix-core backward, bf16, head dim 128: key-outer dK/dV pass and
+// query-outer dQ pass (dq_accum rows written once, unscaled).
+hipError_t launch_bwd_dkdv_d128(const void* Q, const void* K, const void* V, const void* dO,
+                                const float* L, const float* D, void* dK, void* dV, Shape s,
+                                float scale, bool causal, hipStream_t st);
+hipError_t launch_bwd_dq_d128(const void* Q, const void* K, const void* V, const void* dO,
+                              const float* L, const float* D, float* dq_accum, Shape s,
+                              float scale, bool causal, hipStream_t st);
 
 }  // namespace fa

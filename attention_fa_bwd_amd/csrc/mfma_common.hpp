@@ -1,0 +1,104 @@
+// mfma_common.hpp -- CDNA4 (gfx950) matrix-core helpers shared by the two
+// backward kernels (key-outer dK/dV, query-outer dQ).
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the hardware):
+//   A (32 x 16, M x K): lane l holds row l % 32, k = 8 (l / 32) + 0..7
+//   B (16 x 32, K x N): lane l holds column l % 32, k = 8 (l / 32) + 0..7
+//   C (32 x 32):        lane l holds column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4
+//                       for accumulator register r = 0..15
+// ds_read_b64_tr_b16 (per 16-lane group): output lane i, slot s receives
+//   element i % 4 of the 8-byte chunk addressed by lane 4 s + i / 4.
+//
+// A C-layout accumulator can feed a later MFMA as its B operand (or as its A
+// operand, when its columns are the new rows) without any data movement: the
+// contraction index is then permuted the same way on both operands.  Register
+// r = 8 hh + s of a 32-row accumulator is k-slot s of the 16-row step hh and
+// holds row 16 hh + 8 (s / 4) + 4 (l / 32) + s % 4.  The matching operand for
+// the other side is gathered with two transposing LDS reads over rows
+// {16 hh + 4 (l / 32) + 0..3} and {16 hh + 8 + 4 (l / 32) + 0..3}.
+#pragma once
+
+#include "common.hpp"
+
+namespace fa {
+namespace mf {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
+
+#define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int D = 128;       // head dim of the matrix-core kernels
+constexpr int ROWB = D * 2;  // bytes per bf16 row of Q, K, V, dO
+
+__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ bf16x8_t lds_b128(const unsigned char* p) {
+    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+
+// Two transposing 8-byte LDS reads combined into one 8-element operand.
+__device__ __forceinline__ bf16x8_t tr16_pair(const unsigned char* p0, const unsigned char* p1) {
+    i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4_t, p0));
+    i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4_t, p1));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// 16-byte chunk swizzle of a 256-byte row (16 chunks): rows 16 apart repeat,
+// so any 16 consecutive rows read at one logical chunk hit 16 distinct chunks.
+__device__ __forceinline__ int swz(int row) { return row & 15; }
+
+// Byte offset of (row, byte column) in a swizzled 256-byte-row tile.
+__device__ __forceinline__ int tile_off(int row, int colb) {
+    return row * ROWB + ((((colb >> 4) ^ swz(row)) << 4) | (colb & 15));
+}
+
+// Copy rows [r0, r0 + nrows) of a [N, 128] bf16 matrix into a swizzled LDS
+// tile with direct-to-LDS loads: each wave moves 1 KiB (64 lanes x 16 bytes)
+// per instruction, lane i landing at byte 16 i of the wave's slice, so lane i
+// fetches the logical chunk that the swizzle places there.  Rows at or beyond
+// N are clamped to row N - 1 (finite data; callers make them contribute 0).
+template <int NROWS, int NWAVES>
+__device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t* src, int r0,
+                                           int N, int wave, int lane) {
+    constexpr int BYTES = NROWS * ROWB;
+    constexpr int PER_WAVE = BYTES / NWAVES;
+    static_assert(PER_WAVE % 1024 == 0, "tile must split into 1 KiB slices per wave");
+#pragma unroll
+    for (int j = 0; j < PER_WAVE / 1024; ++j) {
+        const int p = wave * PER_WAVE + j * 1024 + lane * 16;
+        const int row = p / ROWB;
+        const int chunk = ((p % ROWB) >> 4) ^ swz(row);
+        int g = r0 + row;
+        g = g < N ? g : N - 1;
+        __builtin_amdgcn_global_load_lds(src + (long long)g * D + chunk * 8,
+                                         FA_LDS(void, lds_tile + wave * PER_WAVE + j * 1024), 16, 0,
+                                         0);
+    }
+}
+
+__device__ __forceinline__ uint4 pack8(const float* v) {
+    uint4 u;
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
+    return u;
+}
+
+// Workgroup id -> work item so that consecutive work items share an XCD
+// (workgroups are dealt to the 8 XCDs round-robin by id).
+__device__ __forceinline__ int xcd_work_item(int bid, int nwork) {
+    return (nwork % 8 == 0) ? (bid % 8) * (nwork / 8) + bid / 8 : bid;
+}
+
+}  // namespace mf
+}  // namespace fa

@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention backward TFLOP/s (10·B·H·N²·d, halved causal) and % bf16 MFMA peak"
-MAIN_KERNEL_SOURCES = ["attention_fa_bwd_amd/csrc/bwd_simt.hip", "attention_fa_bwd_amd/csrc/bwd_mfma.hip"]
+MAIN_KERNEL_SOURCES = ["attention_fa_bwd_amd/csrc/bwd_dkdv.hip", "attention_fa_bwd_amd/csrc/bwd_dq.hip", "attention_fa_bwd_amd/csrc/mfma_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_main_traffic.json")
 
 
