@@ -14,7 +14,8 @@ import torch
 
 __all__ = [
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FAError", "lib_path", "load",
-    "fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq", "fa_strerror",
+    "fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
+    "fa_bwd_convert_dq", "fa_strerror",
     "forward", "backward",
 ]
 
@@ -32,6 +33,8 @@ _SIGS = {
     "fa_fwd_lse": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_preprocess": [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp],
     "fa_bwd": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
+    "fa_bwd_dkdv": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
+    "fa_bwd_dq": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_convert_dq": [_i, _vp, _vp, _i, _i, _i, _i, _f, _vp],
     "fa_last_hip_error": [],
 }
@@ -134,6 +137,26 @@ def fa_bwd(q, k, v, do, L, D, dq_accum, dk, dv, scale: float, causal: bool, stre
                        _ptr(dq_accum, torch.float32), _ptr(dk, q.dtype), _ptr(dv, q.dtype),
                        B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
     _check("fa_bwd", rc)
+
+
+def fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    dt = _dtype_code(q)
+    rc = load().fa_bwd_dkdv(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
+                            _ptr(do, q.dtype), _ptr(L, torch.float32), _ptr(D, torch.float32),
+                            _ptr(dk, q.dtype), _ptr(dv, q.dtype), B, H, N, d, float(scale),
+                            int(bool(causal)), _stream(stream))
+    _check("fa_bwd_dkdv", rc)
+
+
+def fa_bwd_dq(q, k, v, do, L, D, dq_accum, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    dt = _dtype_code(q)
+    rc = load().fa_bwd_dq(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
+                          _ptr(do, q.dtype), _ptr(L, torch.float32), _ptr(D, torch.float32),
+                          _ptr(dq_accum, torch.float32), B, H, N, d, float(scale),
+                          int(bool(causal)), _stream(stream))
+    _check("fa_bwd_dq", rc)
 
 
 def fa_bwd_convert_dq(dq_accum, dq, scale: float, stream=None) -> None:

@@ -22,9 +22,6 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # fp32 atomicAdd lowers to the hardware global_atomic_add_f32
     "-munsafe-fp-atomics",
-    # matrix-core results in VGPRs (the VALU reads S and dP directly); the
-    # allocator then keeps loop-invariant MFMA operands in AGPRs
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -82,6 +82,28 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
                                           causal != 0, st));
 }
 
+int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+                const float* L, const float* D, void* dK, void* dV, int B, int H, int N, int d,
+                float scale, int causal, void* stream) {
+    int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dK, dV});
+    if (rc != FA_OK) return rc;
+    if (!(dtype == FA_DTYPE_BF16 && d == 128)) return FA_EUNSUPPORTED;
+    if ((rc = device_ready()) != FA_OK) return rc;
+    return hip_status(fa::launch_bwd_dkdv_d128(Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d},
+                                               scale, causal != 0, (hipStream_t)stream));
+}
+
+int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+              const float* L, const float* D, float* dq_accum, int B, int H, int N, int d,
+              float scale, int causal, void* stream) {
+    int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum});
+    if (rc != FA_OK) return rc;
+    if (!(dtype == FA_DTYPE_BF16 && d == 128)) return FA_EUNSUPPORTED;
+    if ((rc = device_ready()) != FA_OK) return rc;
+    return hip_status(fa::launch_bwd_dq_d128(Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d},
+                                             scale, causal != 0, (hipStream_t)stream));
+}
+
 int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ, int B, int H, int N, int d,
                       float scale, void* stream) {
     int rc = check(dtype, B, H, N, d, {dq_accum, dQ});

@@ -134,6 +134,7 @@ __device__ __forceinline__ void tile_step(const unsigned char* smem, int buf, in
             accdK[db] = mfma(tr16_pair(sQ + o0, sQ + o1), dSb[t >> 1][t & 1], accdK[db]);
         }
     }
+
 }
 
 template <bool CAUSAL>

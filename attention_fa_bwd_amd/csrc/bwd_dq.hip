@@ -94,6 +94,7 @@ __device__ __forceinline__ void block_step(const unsigned char* smem, int buf, i
                            tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb)), acc[db]);
         }
     }
+
 }
 
 template <bool CAUSAL>

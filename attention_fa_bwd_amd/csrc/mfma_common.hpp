@@ -52,9 +52,14 @@ __device__ __forceinline__ bf16x8_t tr16_pair(const unsigned char* p0, const uns
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 16-byte chunk swizzle of a 256-byte row (16 chunks): rows 16 apart repeat,
-// so any 16 consecutive rows read at one logical chunk hit 16 distinct chunks.
-__device__ __forceinline__ int swz(int row) { return row & 15; }
+// 16-byte chunk swizzle of a 256-byte row (16 chunks), XORed into the chunk
+// index.  LDS has 64 banks of 4 bytes (256 bytes per cycle).  The row-wise
+// operand reads (ds_read_b128: 16 lanes, 16 consecutive rows, one logical
+// chunk) need the 16 rows on 16 distinct chunks; the transposing reads
+// (4 consecutive rows x one 64-byte group of 4 chunks per 32 lanes) need the 4
+// rows on 4 distinct 64-byte groups.  Bits [3:2] of the XOR therefore come from
+// row bits [1:0] and bits [1:0] from row bits [3:2].
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // Byte offset of (row, byte column) in a swizzled 256-byte-row tile.
 __device__ __forceinline__ int tile_off(int row, int colb) {

@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the FlashAttention-2 backward on one MI355X.
 
-A step is one pass of the whole backward hot path -- fa_bwd_preprocess (D and
-dq_accum := 0), fa_bwd (main kernel) and fa_bwd_convert_dq -- over one batch
-of synthetic inputs already resident in HBM.  The forward that produces O and
+A step is one pass of the whole backward hot path -- fa_bwd_preprocess (D),
+the two passes of fa_bwd (fa_bwd_dq, then fa_bwd_dkdv) and fa_bwd_convert_dq --
+over one batch of synthetic inputs already resident in HBM.  The forward that produces O and
 L runs once before timing and is not timed.
 
 Workload (default): B=1, H=32, N=8192, d=128, bf16, non-causal; the causal
@@ -58,14 +58,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, causal: bool):
-    """HBM bytes per main-kernel launch from committed rocprofv3 counter runs,
+def load_traffic(workload: str, causal: bool, kernel: str):
+    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs,
     or None when they are missing or were taken on other kernel sources."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    key = f"{workload}_{'causal' if causal else 'full'}"
+    key = f"{kernel}/{workload}_{'causal' if causal else 'full'}"
     ent = rec.get("entries", {}).get(key)
     if not ent or rec.get("kernel_source_hash") != kernel_source_hash():
         return None
@@ -84,6 +84,12 @@ def calibrate_copy():
                       "launches": 5}))
 
 
+# Algorithmic FLOPs of each backward kernel per (b, h), before the causal halving:
+# the dK/dV pass recomputes S and dP and forms dV and dK (4 of the 5 products),
+# the dQ pass recomputes S and dP and forms dQ (3 products).
+KERNEL_FLOP_FACTOR = {"fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
+
+
 def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     import torch
 
@@ -96,24 +102,29 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
+    # one step: preprocess, dQ pass, dK/dV pass, convert (fa_bwd runs the two
+    # passes back to back; calling them separately lets events split them)
     def step(evs=None):
         if evs:
             evs[0].record(stream)
         fa.fa_bwd_preprocess(o, do, D, dqa, stream)
         if evs:
             evs[1].record(stream)
-        fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, scale, causal, stream)
+        fa.fa_bwd_dq(q, k, v, do, L, D, dqa, scale, causal, stream)
         if evs:
             evs[2].record(stream)
-        fa.fa_bwd_convert_dq(dqa, dq, scale, stream)
+        fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, scale, causal, stream)
         if evs:
             evs[3].record(stream)
+        fa.fa_bwd_convert_dq(dqa, dq, scale, stream)
+        if evs:
+            evs[4].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # timed region: K whole steps; HIP events on the launch stream split it per kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -125,15 +136,14 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    pre = [e[0].elapsed_time(e[1]) for e in evs]
-    main = [e[1].elapsed_time(e[2]) for e in evs]
-    conv = [e[2].elapsed_time(e[3]) for e in evs]
+    split = {name: [e[j].elapsed_time(e[j + 1]) for e in evs]
+             for j, name in enumerate(("fa_bwd_preprocess", "fa_bwd_dq", "fa_bwd_dkdv",
+                                       "fa_bwd_convert_dq"))}
     return {
         "ms_per_step": total_ms / steps,
         "wall_ms_per_step": 1e3 * wall / steps,
-        "main_ms_mean": statistics.fmean(main), "main_ms_min": min(main),
-        "main_ms_median": statistics.median(main),
-        "pre_ms_mean": statistics.fmean(pre), "conv_ms_mean": statistics.fmean(conv),
+        "kernel_ms": {k: statistics.fmean(v) for k, v in split.items()},
+        "kernel_ms_min": {k: min(v) for k, v in split.items()},
     }
 
 
@@ -187,12 +197,18 @@ def main():
         flops = wl.flops(causal)
         r["tflops"] = flops / (r["ms_per_step"] * 1e-3) / 1e12
         r["pct_peak"] = 100.0 * r["tflops"] / PEAK_BF16_TFLOPS
-        r["main_tflops"] = flops / (r["main_ms_mean"] * 1e-3) / 1e12
+        r["kernels"] = {}
+        for name, fac in KERNEL_FLOP_FACTOR.items():
+            kflop = fac / 10.0 * flops
+            ms = r["kernel_ms"][name]
+            r["kernels"][name] = {"avg_launch_ms": round(ms, 4), "flop_per_launch": kflop,
+                                  "achieved": round(kflop / (ms * 1e-3) / 1e12, 3),
+                                  "frac": round(kflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
         results[causal] = r
         del o, L
     prim = results[args.causal]
-    traffic = load_traffic(args.workload, args.causal)
-    main_achieved = prim["main_tflops"]
+    dom = max(KERNEL_FLOP_FACTOR, key=lambda n: prim["kernel_ms"][n])
+    kd = prim["kernels"][dom]
     line = {
         "metric": METRIC,
         "value": round(prim["tflops"], 3),
@@ -211,21 +227,21 @@ def main():
                    "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": args.causal,
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(prim["pct_peak"], 2),
-        "split_ms": {"preprocess": round(prim["pre_ms_mean"], 4), "main": round(prim["main_ms_mean"], 4),
-                     "convert": round(prim["conv_ms_mean"], 4)},
-        "roofline": {"bound": "mfma", "kernel": "fa_bwd main kernel",
-                     "achieved": round(main_achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(main_achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "flop_per_launch": wl.flops(args.causal),
-                     "avg_launch_ms": round(prim["main_ms_mean"], 4)},
+        "split_ms": {k: round(v, 4) for k, v in prim["kernel_ms"].items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": kd["achieved"],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
+                     "traffic": load_traffic(args.workload, args.causal, dom),
+                     "flop_per_launch": kd["flop_per_launch"],
+                     "avg_launch_ms": kd["avg_launch_ms"]},
+        "kernels": prim["kernels"],
     }
     if len(results) > 1:
         other = results[not args.causal]
         line["causal" if not args.causal else "non_causal"] = {
             "value": round(other["tflops"], 3), "ms_per_step": round(other["ms_per_step"], 4),
             "pct_bf16_peak": round(other["pct_peak"], 2),
-            "main_ms": round(other["main_ms_mean"], 4),
-            "main_frac": round(other["main_tflops"] / PEAK_BF16_TFLOPS, 4)}
+            "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
+            "kernels": other["kernels"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
     else:

@@ -85,26 +85,51 @@ int fa_bwd_preprocess(int dtype, const void* O, const void* dO,
                       int B, int H, int N, int d, void* stream);
 
 /*
- * fa_bwd -- the main backward kernel (FA2 chapter 16 sec 16.2 loop order,
- * sec 16.6 skeleton): one workgroup per (key block, head, batch); per query
- * block it recomputes S = scale Q K^T and P = exp(S - L), forms
- * dP = dO V^T and dS = P (dP - D), accumulates dV += P^T dO and
- * dK += dS^T Q in registers, and adds the unscaled dS K into dq_accum with
- * fp32 atomics (sec 16.3, the fp32 accumulation-buffer variant).  Under the
- * causal mask, query blocks wholly above the diagonal are skipped (sec 16.8
- * item 2).  dK is multiplied by `scale` at write-out (sec 16.6).
+ * fa_bwd -- the main backward step (FA2 chapter 16 sec 16.2 loop order, sec
+ * 16.6 skeleton): per (key block, head, batch) it recomputes S = scale Q K^T
+ * and P = exp(S - L), forms dP = dO V^T and dS = P (dP - D), and accumulates
+ * dV = P^T dO and dK = dS^T Q (dK multiplied by `scale` at write-out, sec
+ * 16.6); under the causal mask, tiles wholly above the diagonal are skipped
+ * (sec 16.8 item 2).  dQ = dS K, unscaled, ends up in the fp32 dq_accum buffer
+ * (sec 16.3).
+ *   bf16, d = 128: two matrix-core passes, fa_bwd_dq then fa_bwd_dkdv (below);
+ *                  dq_accum is overwritten, every output is bitwise
+ *                  reproducible.
+ *   other pairs:   one vector-ALU kernel that adds dQ partials into dq_accum
+ *                  with fp32 atomics; dq_accum must hold zeros
+ *                  (fa_bwd_preprocess) and its summation order varies.
  *   in : Q, K, V, dO [B,H,N,d] dtype; L, D [B,H,N] fp32
- *   in/out: dq_accum [B,H,N,d] fp32 -- must hold zeros (fa_bwd_preprocess)
- *           or earlier partial sums; receives += sum_j dS_ij K_j (unscaled)
- *   out: dK, dV [B,H,N,d] dtype
- * dK and dV are bitwise reproducible; dq_accum is a sum of atomics whose order
- * varies from run to run.
+ *   out: dq_accum [B,H,N,d] fp32 = sum_j dS_ij K_j (unscaled);
+ *        dK, dV [B,H,N,d] dtype
  */
 int fa_bwd(int dtype, const void* Q, const void* K, const void* V,
            const void* dO, const float* L, const float* D,
            float* dq_accum, void* dK, void* dV,
            int B, int H, int N, int d, float scale, int causal,
            void* stream);
+
+/*
+ * fa_bwd_dkdv / fa_bwd_dq -- the two passes fa_bwd runs for bf16 with d = 128,
+ * callable on their own (same arguments and layouts as fa_bwd).  FA2 chapter
+ * 16 sec 16.3 weighs fp32 global atomics for dQ against a second kernel; on
+ * MI355X the atomics measured too slow (about 340 G fp32 atomics/s), so dQ has
+ * its own query-outer pass:
+ *   fa_bwd_dkdv: key blocks outer, query tiles inner (sec 16.2); recomputes S,
+ *                P, dP, dS and accumulates dV = P^T dO, dK = scale dS^T Q.
+ *   fa_bwd_dq:   query blocks outer, key blocks inner; recomputes S, P, dP, dS
+ *                and accumulates dQ = dS K, written once (unscaled) into
+ *                dq_accum -- no atomics, bitwise reproducible.
+ * Other dtype / head-dim pairs return FA_EUNSUPPORTED (fa_bwd covers them).
+ */
+int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V,
+                const void* dO, const float* L, const float* D,
+                void* dK, void* dV,
+                int B, int H, int N, int d, float scale, int causal,
+                void* stream);
+int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V,
+              const void* dO, const float* L, const float* D, float* dq_accum,
+              int B, int H, int N, int d, float scale, int causal,
+              void* stream);
 
 /*
  * fa_bwd_convert_dq -- dQ = scale * dq_accum cast to dtype (round to nearest

@@ -149,13 +149,37 @@ def test_max_in_last_key_block():
     assert errs["o"] <= 1e-5
 
 
-def test_dk_dv_bitwise_repeatable():
-    gu.note("case repeatability c2-shaped")
-    inp = si.draw(si.WORKLOADS["c2"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_dk_dv_bitwise_repeatable(d):
+    """dK and dV never use atomics; dQ is reproducible on the matrix-core path
+    (d=128) and within tolerance where atomics reorder its sums (d=64)."""
+    gu.note(f"case repeatability d={d}")
+    inp = si.draw_custom(1, 4, 1024, d, "bf16", seed=1)
     a = gu.run_gpu(inp, True)
     b = gu.run_gpu(inp, True)
     assert torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
-    assert float((a["dq"].float() - b["dq"].float()).abs().max()) <= 1e-2 * float(a["dq"].float().abs().max())
+    if d == 128:
+        assert torch.equal(a["dq"], b["dq"])
+    else:
+        assert float((a["dq"].float() - b["dq"].float()).abs().max()) <= 1e-2 * float(a["dq"].float().abs().max())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_split_passes_equal_fa_bwd(causal):
+    """fa_bwd (bf16, d=128) is exactly fa_bwd_dq followed by fa_bwd_dkdv, and
+    both passes are bitwise reproducible (no atomics)."""
+    import attention_fa_bwd_amd as fa
+    gu.note(f"case split passes causal={causal}")
+    inp = si.draw_custom(1, 3, 700, 128, "bf16", seed=31)
+    out = gu.run_gpu(inp, causal)
+    q, k, v, do, L, D = (out[n] for n in ("q", "k", "v", "do", "L", "D"))
+    dqa = torch.full_like(out["dq_accum"], float("nan"))
+    dk, dv = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+    fa.fa_bwd_dq(q, k, v, do, L, D, dqa, inp.wl.scale, causal)
+    fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, inp.wl.scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dqa, out["dq_accum"])
+    assert torch.equal(dk, out["dk"]) and torch.equal(dv, out["dv"])
 
 
 # ------------------------------------------------------ full-size workloads
