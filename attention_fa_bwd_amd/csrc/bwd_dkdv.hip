@@ -11,21 +11,26 @@
 // above the diagonal are never visited (sec 16.8 item 2).  dQ is produced by
 // the query-outer pass in bwd_dq.hip.
 //
-// gfx950 mapping (4 waves, one per SIMD; wave w owns keys [32 w, 32 w + 32)):
-//   * the K^T and V^T B-operand fragments of S = Q K^T and dP = dO V^T stay in
-//     registers for the whole query loop, as do the dV^T and dK^T accumulators
-//     (32 d x 32 keys x 4 d-blocks each);
-//   * query tiles of 64 rows of Q and dO are double-buffered in LDS (swizzled
-//     256-byte rows) and filled with direct-to-LDS loads one tile ahead;
-//   * S and dP leave the matrix core with the key on the lane, so P and dS are
-//     B operands of dV^T = dO^T P and dK^T = Q^T dS straight from registers;
-//     the transposed A operands dO^T and Q^T come from the same LDS tiles
-//     through ds_read_b64_tr_b16;
-//   * the dP accumulator starts from -D, so it leaves the matrix core as
-//     dP - D; P = exp2(S * scale * log2(e) - L * log2(e)) with L * log2(e)
-//     staged once per tile; rows at or beyond N get L = +inf (P = 0, dS = 0);
-//   * keys at or beyond N need no mask: their P and dS only reach their own
-//     dV / dK rows, which are not stored.
+// gfx950 mapping: 8 waves, two per SIMD, in two roles that overlap on each
+// SIMD (one wave's matrix-core work runs while the other computes or waits on
+// LDS):
+//   * score waves 0..3 own keys [32 s, 32 s + 32).  Their K^T and V^T B-operand
+//     fragments stay in registers; per tile they form S = Q K^T and
+//     dP = dO V^T (query on rows, key on lanes), P = exp2(S scale log2(e) -
+//     L log2(e)) and dS = P (dP - D), and store P and dS (bf16) to LDS in
+//     their own register order, one 1 KiB slab per (16-query step, key group);
+//   * gradient waves 4..7 own rows [32 g, 32 g + 32) of d of dV^T and dK^T for
+//     all 128 keys (accumulators in registers).  One tile behind the score
+//     waves, they read dO^T and Q^T fragments of that tile with
+//     ds_read_b64_tr_b16 -- each fragment feeds four products, one per key
+//     group -- and P and dS straight from the slabs;
+//   * Q and dO tiles (64 rows, swizzled 256-byte rows) rotate through three
+//     LDS buffers (score waves read tile p, gradient waves tile p - 1, loads
+//     fill tile p + 1 with direct-to-LDS copies); P and dS through two.  One
+//     barrier per tile.  LDS: 96 + 64 = 160 KiB;
+//   * rows at or beyond N are staged as copies of row N - 1 and get P = 0;
+//     keys at or beyond N only reach their own dV / dK rows, which are not
+//     stored.
 #include "launch.hpp"
 #include "mfma_common.hpp"
 
@@ -34,111 +39,196 @@ namespace {
 
 using namespace mf;
 
-constexpr int BC = 128;                 // keys per workgroup
-constexpr int BR = 64;                  // queries per tile
-constexpr int NW = 4;                   // waves
-constexpr int TILE = BR * ROWB;         // 16 KiB
-constexpr int OFF_Q = 0;                // 2 buffers
-constexpr int OFF_DO = 2 * TILE;        // 2 buffers
-constexpr int OFF_L = 4 * TILE;         // 2 x BR floats: L * log2(e)
-constexpr int OFF_ND = OFF_L + 2 * BR * 4;  // 2 x BR floats: -D
-constexpr int LDS_BYTES = OFF_ND + 2 * BR * 4;
+constexpr int BC = 128;                  // keys per workgroup
+constexpr int BR = 64;                   // queries per tile
+constexpr int NWAVE = 8;
+constexpr int TILE = BR * ROWB;          // 16 KiB
+constexpr int SLAB = 1024;               // one 16-query x 32-key bf16 operand, lane order
+constexpr int PDS = 4 * 4 * SLAB;        // P (or dS) of one tile: 16 KiB
+constexpr int OFF_Q = 0;                 // 3 buffers
+constexpr int OFF_DO = 3 * TILE;         // 3 buffers
+constexpr int OFF_P = 6 * TILE;          // 2 buffers
+constexpr int OFF_DS = OFF_P + 2 * PDS;  // 2 buffers
+constexpr int LDS_BYTES = OFF_DS + 2 * PDS;
+static_assert(LDS_BYTES == 160 * 1024, "LDS plan");
 
-// Issue the loads of query tile q0 into buffer `buf` (Q, dO direct to LDS;
-// L and D into registers of waves 0 and 1, written to LDS by put_rowstats).
-__device__ __forceinline__ float stage_tile(unsigned char* smem, int buf, const bf16_t* Qh,
-                                            const bf16_t* dOh, const float* Lh, const float* Dh,
-                                            int q0, int N, int w, int l) {
-    stage_rows<BR, NW>(smem + OFF_Q + buf * TILE, Qh, q0, N, w, l);
-    stage_rows<BR, NW>(smem + OFF_DO + buf * TILE, dOh, q0, N, w, l);
-    float v = 0.f;
-    const int q = q0 + l;
-    if (w == 0) v = q < N ? Lh[q] * kLog2e : INFINITY;
-    if (w == 1) v = q < N ? -Dh[q] : 0.f;
-    return v;
+// L and D of the 16 query rows a lane holds in 32-row block qb of the tile:
+// rows 32 qb + 8 a4 + 4 h + 0..3, four consecutive per load.  Rows at or
+// beyond N (RAGGED tiles only) get L = +inf, so their P is 0.
+template <bool RAGGED>
+__device__ __forceinline__ void load_rowstats(f32x4_t (&Lv)[4], f32x4_t (&Dv)[4], const float* Lh,
+                                              const float* Dh, int q0, int qb, int N, int h) {
+    const f32x4_t* Lrow = reinterpret_cast<const f32x4_t*>(Lh + q0 + 4 * h);
+    const f32x4_t* Drow = reinterpret_cast<const f32x4_t*>(Dh + q0 + 4 * h);
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        if (!RAGGED) {
+            Lv[a4] = Lrow[8 * qb + 2 * a4];
+            Dv[a4] = Drow[8 * qb + 2 * a4];
+        } else {
+            const int q = q0 + 32 * qb + 8 * a4 + 4 * h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int qc = q + e < N ? q + e : N - 1;
+                Lv[a4][e] = q + e < N ? Lh[qc] : INFINITY;
+                Dv[a4][e] = q + e < N ? Dh[qc] : 0.f;
+            }
+        }
+    }
 }
 
-__device__ __forceinline__ void put_rowstats(unsigned char* smem, int buf, float v, int w, int l) {
-    if (w == 0) reinterpret_cast<float*>(smem + OFF_L)[buf * BR + l] = v;
-    if (w == 1) reinterpret_cast<float*>(smem + OFF_ND)[buf * BR + l] = v;
-}
-
+// P and dS of accumulator elements r, r + 1 (one packed bf16 pair each).
 template <bool MASK>
-__device__ __forceinline__ void tile_step(const unsigned char* smem, int buf, int q0, int key,
-                                          float sc, const bf16x8_t (&kt)[8],
-                                          const bf16x8_t (&vt)[8], f32x16_t (&accdV)[4],
-                                          f32x16_t (&accdK)[4], int l) {
-    const int h = l >> 5, n = l & 31, g2 = (l >> 4) & 1;
-    const unsigned char* sQ = smem + OFF_Q + buf * TILE;
-    const unsigned char* sdO = smem + OFF_DO + buf * TILE;
-    const float* sL = reinterpret_cast<const float*>(smem + OFF_L) + buf * BR;
-    const float* sND = reinterpret_cast<const float*>(smem + OFF_ND) + buf * BR;
+__device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP,
+                                         const f32x4_t (&Lv)[4], const f32x4_t (&Dv)[4], int r,
+                                         float sc, int key, int qrow, uint32_t& pp, uint32_t& pd) {
+    float p[2], d[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = r + u;
+        float x = __builtin_fmaf(S[e], sc, Lv[e >> 2][e & 3] * -kLog2e);
+        if (MASK && key > qrow + 8 * (e >> 2) + (e & 3)) x = -INFINITY;
+        p[u] = __builtin_amdgcn_exp2f(x);
+        d[u] = p[u] * (dP[e] - Dv[e >> 2][e & 3]);
+    }
+    pp = pack_bf16x2(p[0], p[1]);
+    pd = pack_bf16x2(d[0], d[1]);
+}
 
-    // S = Q K^T and dP - D = dO V^T - D; query on rows, key on lanes
-    f32x16_t S[2], dP[2];
+// Score role on a diagonal tile (causal mask applied element by element):
+// block by block, no interleaving -- two such tiles per workgroup, and the
+// mask needs registers the interleaved order does not have to spare.
+template <bool RAGGED>
+__device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, int pbuf, int q0,
+                                                int N, int key, float sc, const float* Lh,
+                                                const float* Dh, const bf16x8_t (&kt)[8],
+                                                const bf16x8_t (&vt)[8], int s, int l) {
+    const int h = l >> 5, n = l & 31;
+    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
+    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
+    unsigned char* sP = smem + OFF_P + pbuf * PDS;
+    unsigned char* sS = smem + OFF_DS + pbuf * PDS;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        f32x4_t nd[4];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4)
-            nd[a4] = *reinterpret_cast<const f32x4_t*>(sND + 32 * qb + 8 * a4 + 4 * h);
-        dP[qb] = __builtin_shufflevector(
-            __builtin_shufflevector(nd[0], nd[1], 0, 1, 2, 3, 4, 5, 6, 7),
-            __builtin_shufflevector(nd[2], nd[3], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2, 3, 4, 5, 6, 7,
-            8, 9, 10, 11, 12, 13, 14, 15);
-        S[qb] = f32x16_t{};
+        f32x4_t Lv[4], Dv[4];
+        load_rowstats<RAGGED>(Lv, Dv, Lh, Dh, q0, qb, N, h);
+        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
         const int row = 32 * qb + n;
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
             const int off = tile_off(row, 32 * dk + 16 * h);
-            S[qb] = mfma(lds_b128(sQ + off), kt[dk], S[qb]);
-            dP[qb] = mfma(lds_b128(sdO + off), vt[dk], dP[qb]);
+            S = mfma(lds_b128(sQ + off), kt[dk], S);
+            dP = mfma(lds_b128(sdO + off), vt[dk], dP);
         }
-    }
-
-    // P = exp2(S sc - L'), dS = P (dP - D), both to bf16
-    bf16x8_t Pb[2][2], dSb[2][2];
+        uint32_t pk[8], dk[8];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        float p[16], ds[16];
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-            const int rq = 32 * qb + 8 * a4 + 4 * h;
-            const f32x4_t Lv = *reinterpret_cast<const f32x4_t*>(sL + rq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 4 * a4 + e;
-                float x = __builtin_fmaf(S[qb][r], sc, -Lv[e]);
-                if (MASK && key > q0 + rq + e) x = -INFINITY;
-                const float pv = __builtin_amdgcn_exp2f(x);
-                p[r] = pv;
-                ds[r] = pv * dP[qb][r];
-            }
-        }
+        for (int j = 0; j < 8; ++j)
+            pds_pair<true>(S, dP, Lv, Dv, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            Pb[qb][hh] = as_bf16x8(pack8(p + 8 * hh));
-            dSb[qb][hh] = as_bf16x8(pack8(ds + 8 * hh));
+            const int slab = ((2 * qb + hh) * 4 + s) * SLAB + l * 16;
+            *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
+            *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
         }
     }
+}
 
-    // dV^T += dO^T P, dK^T += Q^T dS; d on rows, key on lanes
+// Score role: S, dP, P, dS of query tile q0 (below the causal diagonal, or
+// any tile without the mask) for this wave's 32 keys.  RAGGED: the tile runs
+// past row N.  Issue order (pinned with sched_barrier): operand reads run two
+// MFMA pairs ahead; the S/dP products of block 1 are interleaved with the P/dS
+// arithmetic of block 0; block 1's arithmetic then overlaps the gradient wave
+// sharing the SIMD.
+template <bool RAGGED>
+__device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pbuf, int q0, int N,
+                                           int key, float sc, const float* Lh, const float* Dh,
+                                           const bf16x8_t (&kt)[8], const bf16x8_t (&vt)[8],
+                                           int s, int l) {
+    const int h = l >> 5, n = l & 31;
+    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
+    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
+    unsigned char* sP = smem + OFF_P + pbuf * PDS;
+    unsigned char* sS = smem + OFF_DS + pbuf * PDS;
+
+    f32x4_t Lv0[4], Dv0[4], Lv1[4], Dv1[4];
+    load_rowstats<RAGGED>(Lv0, Dv0, Lh, Dh, q0, 0, N, h);
+
+    // operand of step i (i = 0..15: block i / 8, d-chunk i % 8)
+    auto opoff = [&](int i) { return tile_off(32 * (i >> 3) + n, 32 * (i & 7) + 16 * h); };
+    bf16x8_t aq[3], ag[3];
+    aq[0] = lds_b128(sQ + opoff(0));
+    ag[0] = lds_b128(sdO + opoff(0));
+    aq[1] = lds_b128(sQ + opoff(1));
+    ag[1] = lds_b128(sdO + opoff(1));
+
+    f32x16_t S0 = f32x16_t{}, dP0 = f32x16_t{}, S1 = f32x16_t{}, dP1 = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
+        ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
+        S0 = mfma(aq[i % 3], kt[i], S0);
+        dP0 = mfma(ag[i % 3], vt[i], dP0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t pk[8], dk[8];
+    const int qrow0 = q0 + 4 * h, qrow1 = q0 + 32 + 4 * h;
+    load_rowstats<RAGGED>(Lv1, Dv1, Lh, Dh, q0, 1, N, h);
+#pragma unroll
+    for (int i = 8; i < 16; ++i) {
+        if (i + 2 < 16) {
+            aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
+            ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
+        }
+        S1 = mfma(aq[i % 3], kt[i - 8], S1);
+        dP1 = mfma(ag[i % 3], vt[i - 8], dP1);
+        pds_pair<false>(S0, dP0, Lv0, Dv0, 2 * (i - 8), sc, key, qrow0, pk[i - 8], dk[i - 8]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int slab = (hh * 4 + s) * SLAB + l * 16;
+        *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
+        *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        pds_pair<false>(S1, dP1, Lv1, Dv1, 2 * j, sc, key, qrow1, pk[j], dk[j]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int slab = ((2 + hh) * 4 + s) * SLAB + l * 16;
+        *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
+        *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
+    }
+}
+
+// Gradient role: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 rows of d.
+__device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf,
+                                          f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int g,
+                                          int l) {
+    const int h = l >> 5, g2 = (l >> 4) & 1;
+    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
+    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
+    const unsigned char* sP = smem + OFF_P + pbuf * PDS;
+    const unsigned char* sS = smem + OFF_DS + pbuf * PDS;
+    const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
+        const int o0 = tile_off(r0, colb), o1 = tile_off(r0 + 8, colb);
+        const bf16x8_t aO = tr16_pair(sdO + o0, sdO + o1);
+        const bf16x8_t aQ = tr16_pair(sQ + o0, sQ + o1);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int colb = 64 * db + 32 * g2 + 8 * (l & 3);
-            const int o0 = tile_off(r0, colb), o1 = tile_off(r0 + 8, colb);
-            accdV[db] = mfma(tr16_pair(sdO + o0, sdO + o1), Pb[t >> 1][t & 1], accdV[db]);
-            accdK[db] = mfma(tr16_pair(sQ + o0, sQ + o1), dSb[t >> 1][t & 1], accdK[db]);
+        for (int kg = 0; kg < 4; ++kg) {
+            const int slab = (t * 4 + kg) * SLAB + l * 16;
+            accdV[kg] = mfma(aO, lds_b128(sP + slab), accdV[kg]);
+            accdK[kg] = mfma(aQ, lds_b128(sS + slab), accdK[kg]);
         }
     }
-
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int nkb, float scale) {
@@ -153,61 +243,93 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const float* Lh = Lg + (long long)head * N;
     const float* Dh = Dg + (long long)head * N;
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
-    const int key = k0 + 32 * w + n;
-    const int keyc = key < N ? key : N - 1;  // clamped: finite data, outputs not stored
-
-    bf16x8_t kt[8], vt[8];
-#pragma unroll
-    for (int dk = 0; dk < 8; ++dk) {
-        kt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
-        vt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
-    }
-    f32x16_t accdV[4], accdK[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) accdV[i] = accdK[i] = f32x16_t{};
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
+    const bool score = wave < 4;
+    const int r4 = wave & 3;  // key group (score) or d block (gradient)
+    const int key = k0 + 32 * r4 + n;
 
     const int q_begin = CAUSAL ? k0 : 0;
     const int ntiles = (N - q_begin + BR - 1) / BR;
     const int nmask = CAUSAL ? BC / BR : 0;  // tiles that cross the diagonal
     const float sc = scale * kLog2e;
 
-    float rs = stage_tile(smem, 0, Qh, dOh, Lh, Dh, q_begin, N, w, l);
-    put_rowstats(smem, 0, rs, w, l);
+    stage_rows<BR, NWAVE>(smem + OFF_Q, Qh, q_begin, N, wave, l);
+    stage_rows<BR, NWAVE>(smem + OFF_DO, dOh, q_begin, N, wave, l);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int buf = it & 1;
-        const int q0 = q_begin + it * BR;
-        const bool more = it + 1 < ntiles;
-        if (more) rs = stage_tile(smem, buf ^ 1, Qh, dOh, Lh, Dh, q0 + BR, N, w, l);
-        if (it < nmask)
-            tile_step<true>(smem, buf, q0, key, sc, kt, vt, accdV, accdK, l);
-        else
-            tile_step<false>(smem, buf, q0, key, sc, kt, vt, accdV, accdK, l);
-        if (more) put_rowstats(smem, buf ^ 1, rs, w, l);
+    // Phase p (one barrier each, ntiles + 1 phases): score waves work on tile p;
+    // gradient waves stage tile p + 1 (the score waves' only memory traffic is
+    // L and D, so their waits never cover the staging copies) and work on
+    // tile p - 1.  Each role has its own loop so that its registers never
+    // coexist with the other role's.
+    if (score) {
+        const int keyc = key < N ? key : N - 1;  // clamped: finite data, outputs not stored
+        bf16x8_t kt[8], vt[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) {
+            kt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
+            vt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
+        }
+        // diagonal tiles (causal only) in a loop of their own, then the rest
+        int p = 0;
+        for (; p < min(nmask, ntiles); ++p) {
+            const int q0 = q_begin + p * BR;
+            if (q0 + BR > N)
+                score_step_diag<true>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+            else
+                score_step_diag<false>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        for (; p <= ntiles; ++p) {
+            if (p < ntiles) {
+                const int q0 = q_begin + p * BR;
+                if (q0 + BR > N)
+                    score_step<true>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+                else
+                    score_step<false>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+
+    f32x16_t accdV[4], accdK[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) accdV[i] = accdK[i] = f32x16_t{};
+    for (int p = 0; p <= ntiles; ++p) {
+        if (p + 1 < ntiles) {
+            const int b = (p + 1) % 3;
+            stage_rows<BR, NWAVE / 2>(smem + OFF_Q + b * TILE, Qh, q_begin + (p + 1) * BR, N, r4, l);
+            stage_rows<BR, NWAVE / 2>(smem + OFF_DO + b * TILE, dOh, q_begin + (p + 1) * BR, N, r4, l);
+        }
+        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, r4, l);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    if (key < N) {
-        bf16_t* dKr = dK + hoff + (long long)key * D;
-        bf16_t* dVr = dV + hoff + (long long)key * D;
+    // epilogue: accumulator kg holds dV^T / dK^T for keys k0 + 32 kg + n,
+    // rows of d 32 g + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+    for (int kg = 0; kg < 4; ++kg) {
+        const int kk = k0 + 32 * kg + n;
+        if (kk >= N) continue;
+        bf16_t* dKr = dK + hoff + (long long)kk * D;
+        bf16_t* dVr = dV + hoff + (long long)kk * D;
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d0 = 32 * db + 8 * a4 + 4 * h;
-                const int r = 4 * a4;
-                uint2 kv, vv;
-                kv.x = pack_bf16x2(accdK[db][r] * scale, accdK[db][r + 1] * scale);
-                kv.y = pack_bf16x2(accdK[db][r + 2] * scale, accdK[db][r + 3] * scale);
-                vv.x = pack_bf16x2(accdV[db][r], accdV[db][r + 1]);
-                vv.y = pack_bf16x2(accdV[db][r + 2], accdV[db][r + 3]);
-                *reinterpret_cast<uint2*>(dKr + d0) = kv;
-                *reinterpret_cast<uint2*>(dVr + d0) = vv;
-            }
+        for (int a4 = 0; a4 < 4; ++a4) {
+            const int d0 = 32 * r4 + 8 * a4 + 4 * h;
+            const int r = 4 * a4;
+            uint2 kv, vv;
+            kv.x = pack_bf16x2(accdK[kg][r] * scale, accdK[kg][r + 1] * scale);
+            kv.y = pack_bf16x2(accdK[kg][r + 2] * scale, accdK[kg][r + 3] * scale);
+            vv.x = pack_bf16x2(accdV[kg][r], accdV[kg][r + 1]);
+            vv.y = pack_bf16x2(accdV[kg][r + 2], accdV[kg][r + 3]);
+            *reinterpret_cast<uint2*>(dKr + d0) = kv;
+            *reinterpret_cast<uint2*>(dVr + d0) = vv;
+        }
     }
 }
 
@@ -221,13 +343,13 @@ hipError_t launch_bwd_dkdv_d128(const void* Q, const void* K, const void* V, con
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<true>), grid, dim3(NW * 64), 0, st, (const bf16_t*)Q,
-                           (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv,
-                           (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<true>), grid, dim3(NWAVE * 64), 0, st,
+                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO,
+                           L, Dv, (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)Q,
-                           (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv,
-                           (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<false>), grid, dim3(NWAVE * 64), 0, st,
+                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO,
+                           L, Dv, (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
     return hipGetLastError();
 }
 

@@ -11,16 +11,21 @@
 // dq_accum row is written once, with plain stores.  Under the causal mask the
 // key loop stops at the diagonal (sec 16.8 item 2).
 //
-// gfx950 mapping (4 waves, one per SIMD; wave w owns queries [32 w, 32 w + 32)):
-//   * the Q^T and dO^T B-operand fragments of S^T = K Q^T and dP^T = V dO^T
-//     stay in registers for the whole key loop, as do L * log2(e) and -D of the
-//     lane's query row, and the dQ accumulator (32 queries x 128 d);
-//   * key blocks of 64 rows of K and V are double-buffered in LDS (swizzled
-//     256-byte rows), filled one block ahead with direct-to-LDS loads;
-//   * S^T and dP^T leave the matrix core with the query on the lane, so dS is
-//     the A operand of dQ = dS K straight from registers; the K operand with
-//     the key on the contraction index comes from the same LDS tile through
-//     ds_read_b64_tr_b16;
+// gfx950 mapping: 8 waves, two per SIMD, in two roles that overlap on each
+// SIMD:
+//   * score waves 0..3 own queries [32 s, 32 s + 32) of the block; their Q^T
+//     and dO^T B-operand fragments, L and D stay in registers.  Per key block
+//     of 64 they form S^T = K Q^T and dP^T = V dO^T (key on rows, query on
+//     lanes) and dS = P (dP - D), and store dS (bf16) to LDS in their own
+//     register order, one 1 KiB slab per (16-key step, query group);
+//   * gradient waves 4..7 own columns [32 g, 32 g + 32) of d of dQ for all
+//     128 queries (accumulators in registers).  One key block behind, they
+//     read the K operand of that block (key on the contraction index) with
+//     ds_read_b64_tr_b16 -- each fragment feeds four products, one per query
+//     group -- and dS straight from the slabs;
+//   * K blocks rotate through three LDS buffers (score waves read block p,
+//     gradient waves block p - 1, loads fill block p + 1 with direct-to-LDS
+//     copies), V blocks through two, dS through two.  One barrier per block;
 //   * rows at or beyond N are staged as copies of row N - 1; in the last key
 //     block their P is forced to 0, and query rows at or beyond N are not
 //     stored.
@@ -32,73 +37,75 @@ namespace {
 
 using namespace mf;
 
-constexpr int BQ = 128;                 // queries per workgroup
-constexpr int BK = 64;                  // keys per block
-constexpr int NW = 4;                   // waves
-constexpr int TILE = BK * ROWB;         // 16 KiB
-constexpr int OFF_K = 0;                // 2 buffers
-constexpr int OFF_V = 2 * TILE;         // 2 buffers
-constexpr int LDS_BYTES = 4 * TILE;
+constexpr int BQ = 128;                  // queries per workgroup
+constexpr int BK = 64;                   // keys per block
+constexpr int NWAVE = 8;
+constexpr int TILE = BK * ROWB;          // 16 KiB
+constexpr int SLAB = 1024;               // one 32-query x 16-key bf16 operand, lane order
+constexpr int DSB = 4 * 4 * SLAB;        // dS of one block: 16 KiB
+constexpr int OFF_K = 0;                 // 3 buffers
+constexpr int OFF_V = 3 * TILE;          // 2 buffers
+constexpr int OFF_DS = 5 * TILE;         // 2 buffers
+constexpr int LDS_BYTES = OFF_DS + 2 * DSB;
 
-// MASK: apply key > query (causal) and key >= N (last block) element by element.
+// Score role: dS of key block k0 for this wave's 32 queries.  MASK applies
+// key > query (causal) and key >= N element by element.
 template <bool MASK, bool CAUSAL>
-__device__ __forceinline__ void block_step(const unsigned char* smem, int buf, int k0, int q, int N,
-                                           float sc, float Lq, const f32x16_t& negD,
+__device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vbuf, int dbuf,
+                                           int k0, int q, int N, float sc, float Lq, float Dq,
                                            const bf16x8_t (&qt)[8], const bf16x8_t (&gt)[8],
-                                           f32x16_t (&acc)[4], int l) {
-    const int h = l >> 5, n = l & 31, g2 = (l >> 4) & 1;
-    const unsigned char* sK = smem + OFF_K + buf * TILE;
-    const unsigned char* sV = smem + OFF_V + buf * TILE;
-
-    // S^T = K Q^T and dP^T - D = V dO^T - D; key on rows, query on lanes
-    f32x16_t S[2], dP[2];
+                                           int s, int l) {
+    const int h = l >> 5, n = l & 31;
+    const unsigned char* sK = smem + OFF_K + kbuf * TILE;
+    const unsigned char* sV = smem + OFF_V + vbuf * TILE;
+    unsigned char* sS = smem + OFF_DS + dbuf * DSB;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        S[mb] = f32x16_t{};
-        dP[mb] = negD;
+        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
         const int row = 32 * mb + n;
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
             const int off = tile_off(row, 32 * dk + 16 * h);
-            S[mb] = mfma(lds_b128(sK + off), qt[dk], S[mb]);
-            dP[mb] = mfma(lds_b128(sV + off), gt[dk], dP[mb]);
+            S = mfma(lds_b128(sK + off), qt[dk], S);
+            dP = mfma(lds_b128(sV + off), gt[dk], dP);
         }
-    }
-
-    // dS = P (dP - D) with P = exp2(S sc - L'), to bf16
-    bf16x8_t dSb[2][2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float x = __builtin_fmaf(S[mb][r], sc, -Lq);
+            float x = __builtin_fmaf(S[r], sc, -Lq);
             if (MASK) {
                 const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
             }
-            ds[r] = __builtin_amdgcn_exp2f(x) * dP[mb][r];
+            ds[r] = __builtin_amdgcn_exp2f(x) * (dP[r] - Dq);
         }
-        dSb[mb][0] = as_bf16x8(pack8(ds));
-        dSb[mb][1] = as_bf16x8(pack8(ds + 8));
+        // slab (t = 2 mb + hh, query group s), lane-ordered 16 bytes
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            *reinterpret_cast<uint4*>(sS + ((2 * mb + hh) * 4 + s) * SLAB + l * 16) =
+                pack8(ds + 8 * hh);
     }
+}
 
-    // dQ += dS K; query on rows, d on lanes
+// Gradient role: dQ[:, 32 g .. 32 g + 31] += dS K for the block's 64 keys.
+__device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, int dbuf,
+                                          f32x16_t (&acc)[4], int g, int l) {
+    const int h = l >> 5, g2 = (l >> 4) & 1;
+    const unsigned char* sK = smem + OFF_K + kbuf * TILE;
+    const unsigned char* sS = smem + OFF_DS + dbuf * DSB;
+    const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
+        const bf16x8_t bK = tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb));
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const int colb = 64 * db + 32 * g2 + 8 * (l & 3);
-            acc[db] = mfma(dSb[t >> 1][t & 1],
-                           tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb)), acc[db]);
-        }
+        for (int qg = 0; qg < 4; ++qg)
+            acc[qg] = mfma(lds_b128(sS + (t * 4 + qg) * SLAB + l * 16), bK, acc[qg]);
     }
-
 }
 
 template <bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
+__global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
     float* __restrict__ dqa, int N, int nqb, float scale) {
@@ -112,58 +119,72 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const bf16_t* Kh = K + hoff;
     const bf16_t* Vh = V + hoff;
 
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
-    const int q = q0 + 32 * w + n;          // this lane's query in S^T / dP^T
-    const int qc = q < N ? q : N - 1;       // clamped: finite data, row not stored
-
-    bf16x8_t qt[8], gt[8];
-#pragma unroll
-    for (int dk = 0; dk < 8; ++dk) {
-        qt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
-        gt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * D + 16 * dk + 8 * h));
-    }
-    const float Lq = Lg[(long long)head * N + qc] * kLog2e;
-    const float nD = -Dg[(long long)head * N + qc];
-    f32x16_t negD;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) negD[r] = nD;
-    f32x16_t acc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
+    const bool score = wave < 4;
+    const int r4 = wave & 3;             // query group (score) or d block (gradient)
+    const int q = q0 + 32 * r4 + n;      // score waves: this lane's query in S^T / dP^T
 
     const int kend = CAUSAL ? min(N, q0 + BQ) : N;
     const int nblk = (kend + BK - 1) / BK;
-    const int full = CAUSAL ? min(q0 / BK, (N / BK)) : N / BK;  // blocks needing no mask
+    const int full = CAUSAL ? min(q0 / BK, N / BK) : N / BK;  // blocks needing no mask
     const float sc = scale * kLog2e;
 
-    stage_rows<BK, NW>(smem + OFF_K, Kh, 0, N, w, l);
-    stage_rows<BK, NW>(smem + OFF_V, Vh, 0, N, w, l);
+    stage_rows<BK, NWAVE>(smem + OFF_K, Kh, 0, N, wave, l);
+    stage_rows<BK, NWAVE>(smem + OFF_V, Vh, 0, N, wave, l);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int it = 0; it < nblk; ++it) {
-        const int buf = it & 1;
-        const int k0 = it * BK;
-        if (it + 1 < nblk) {
-            stage_rows<BK, NW>(smem + OFF_K + (buf ^ 1) * TILE, Kh, k0 + BK, N, w, l);
-            stage_rows<BK, NW>(smem + OFF_V + (buf ^ 1) * TILE, Vh, k0 + BK, N, w, l);
+    // Phase p (one barrier each, nblk + 1 phases): score waves work on block p;
+    // gradient waves stage block p + 1 and work on block p - 1 (the score
+    // waves' MFMA work is twice theirs).  Each role has its own loop so their
+    // registers never coexist.
+    if (score) {
+        const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
+        bf16x8_t qt[8], gt[8];
+#pragma unroll
+        for (int dk = 0; dk < 8; ++dk) {
+            qt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
+            gt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * D + 16 * dk + 8 * h));
         }
-        if (it < full)
-            block_step<false, CAUSAL>(smem, buf, k0, q, N, sc, Lq, negD, qt, gt, acc, l);
-        else
-            block_step<true, CAUSAL>(smem, buf, k0, q, N, sc, Lq, negD, qt, gt, acc, l);
+        const float Lq = Lg[(long long)head * N + qc] * kLog2e;
+        const float Dq = Dg[(long long)head * N + qc];
+        for (int p = 0; p <= nblk; ++p) {
+            if (p < nblk) {
+                if (p < full)
+                    score_step<false, CAUSAL>(smem, p % 3, p & 1, p & 1, p * BK, q, N, sc, Lq, Dq,
+                                              qt, gt, r4, l);
+                else
+                    score_step<true, CAUSAL>(smem, p % 3, p & 1, p & 1, p * BK, q, N, sc, Lq, Dq,
+                                             qt, gt, r4, l);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        return;
+    }
+
+    f32x16_t acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    for (int p = 0; p <= nblk; ++p) {
+        if (p + 1 < nblk) {
+            stage_rows<BK, NWAVE / 2>(smem + OFF_K + ((p + 1) % 3) * TILE, Kh, (p + 1) * BK, N, r4, l);
+            stage_rows<BK, NWAVE / 2>(smem + OFF_V + ((p + 1) & 1) * TILE, Vh, (p + 1) * BK, N, r4, l);
+        }
+        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, acc, r4, l);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // dq_accum[query][d] = acc: lane holds column 32 db + n, rows 8 (r / 4) + 4 h + r % 4
+    // epilogue: acc[qg] holds dQ for queries q0 + 32 qg + 8 (r / 4) + 4 h + r % 4,
+    // column 32 g + n
     float* out = dqa + hoff;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int qg = 0; qg < 4; ++qg)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int qq = q0 + 32 * w + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (qq < N) out[(long long)qq * D + 32 * db + n] = acc[db][r];
+            const int qq = q0 + 32 * qg + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (qq < N) out[(long long)qq * D + 32 * r4 + n] = acc[qg][r];
         }
 }
 
@@ -177,11 +198,11 @@ hipError_t launch_bwd_dq_d128(const void* Q, const void* K, const void* V, const
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<true>), grid, dim3(NW * 64), 0, st, (const bf16_t*)Q,
+        hipLaunchKernelGGL((bwd_dq_kernel<true>), grid, dim3(NWAVE * 64), 0, st, (const bf16_t*)Q,
                            (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv, dqa, s.N,
                            nqb, scale);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<false>), grid, dim3(NW * 64), 0, st, (const bf16_t*)Q,
+        hipLaunchKernelGGL((bwd_dq_kernel<false>), grid, dim3(NWAVE * 64), 0, st, (const bf16_t*)Q,
                            (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv, dqa, s.N,
                            nqb, scale);
     return hipGetLastError();
