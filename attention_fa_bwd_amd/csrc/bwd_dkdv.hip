@@ -52,44 +52,56 @@ constexpr int OFF_DS = OFF_P + 2 * PDS;  // 2 buffers
 constexpr int LDS_BYTES = OFF_DS + 2 * PDS;
 static_assert(LDS_BYTES == 160 * 1024, "LDS plan");
 
-// L and D of the 16 query rows a lane holds in 32-row block qb of the tile:
-// rows 32 qb + 8 a4 + 4 h + 0..3, four consecutive per load.  Rows at or
-// beyond N (RAGGED tiles only) get L = +inf, so their P is 0.
+// Row statistics enter the score products as the accumulators' starting
+// values: S starts at -L / scale and dP at -D, so that P = exp2(S scale log2 e)
+// and dS = P dP need no per-element correction.  Those starting values are
+// made by one matrix-core product per accumulator: the A operand holds, on
+// row n, the value split into three bf16 terms (k-slots 0..2 on lanes of
+// half 0 for S, k-slots 8..10 on lanes of half 1 for dP), the B operand is 1
+// on those k-slots for every column, so the product broadcasts the row's value
+// across the 32 key columns in accumulator layout.  The three terms carry the
+// value to about 2^-26 relative.  Each lane fetches a single float per
+// 32-row block (L of row n on half 0, D of row n on half 1), one tile ahead.
+
+// float of a 32-row block for this lane: L (half 0) or D (half 1) of row q,
+// clamped into [0, N).
+__device__ __forceinline__ float fetch_stat(const float* src, int q, int N) {
+    return src[q < N ? q : N - 1];
+}
+
+// bias operands of one 32-row block from the fetched float; fac is -1/scale
+// on half 0 and -1 on half 1.  RAGGED: row q >= N gets S = -1e30 (P = 0) and
+// dP = 0.
 template <bool RAGGED>
-__device__ __forceinline__ void load_rowstats(f32x4_t (&Lv)[4], f32x4_t (&Dv)[4], const float* Lh,
-                                              const float* Dh, int q0, int qb, int N, int h) {
-    const f32x4_t* Lrow = reinterpret_cast<const f32x4_t*>(Lh + q0 + 4 * h);
-    const f32x4_t* Drow = reinterpret_cast<const f32x4_t*>(Dh + q0 + 4 * h);
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-        if (!RAGGED) {
-            Lv[a4] = Lrow[8 * qb + 2 * a4];
-            Dv[a4] = Drow[8 * qb + 2 * a4];
-        } else {
-            const int q = q0 + 32 * qb + 8 * a4 + 4 * h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int qc = q + e < N ? q + e : N - 1;
-                Lv[a4][e] = q + e < N ? Lh[qc] : INFINITY;
-                Dv[a4][e] = q + e < N ? Dh[qc] : 0.f;
-            }
-        }
-    }
+__device__ __forceinline__ void bias_operands(float raw, int q, int N, int h, float fac,
+                                              bf16x8_t& aS, bf16x8_t& aD) {
+    float u = raw * fac;
+    if (RAGGED && q >= N) u = h ? 0.f : -1e30f;
+    const float hi = (float)(__bf16)u;
+    const float r1 = u - hi;
+    const float mid = (float)(__bf16)r1;
+    const uint32_t w0 = pack_bf16x2(hi, mid), w1 = pack_bf16x2(r1 - mid, 0.f);
+    aS = as_bf16x8(h ? make_uint4(0, 0, 0, 0) : make_uint4(w0, w1, 0, 0));
+    aD = as_bf16x8(h ? make_uint4(w0, w1, 0, 0) : make_uint4(0, 0, 0, 0));
+}
+
+// 1.0 on k-slots 0..2 of every lane: B operand of the bias products
+__device__ __forceinline__ bf16x8_t bias_ones() {
+    return as_bf16x8(make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
 }
 
 // P and dS of accumulator elements r, r + 1 (one packed bf16 pair each).
 template <bool MASK>
-__device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP,
-                                         const f32x4_t (&Lv)[4], const f32x4_t (&Dv)[4], int r,
-                                         float sc, int key, int qrow, uint32_t& pp, uint32_t& pd) {
+__device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
+                                         int key, int qrow, uint32_t& pp, uint32_t& pd) {
     float p[2], d[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int e = r + u;
-        float x = __builtin_fmaf(S[e], sc, Lv[e >> 2][e & 3] * -kLog2e);
+        float x = S[e] * sc;
         if (MASK && key > qrow + 8 * (e >> 2) + (e & 3)) x = -INFINITY;
         p[u] = __builtin_amdgcn_exp2f(x);
-        d[u] = p[u] * (dP[e] - Dv[e >> 2][e & 3]);
+        d[u] = p[u] * dP[e];
     }
     pp = pack_bf16x2(p[0], p[1]);
     pd = pack_bf16x2(d[0], d[1]);
@@ -100,19 +112,20 @@ __device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP,
 // mask needs registers the interleaved order does not have to spare.
 template <bool RAGGED>
 __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, int pbuf, int q0,
-                                                int N, int key, float sc, const float* Lh,
-                                                const float* Dh, const bf16x8_t (&kt)[8],
+                                                int N, int key, float sc, float fac,
+                                                const float (&st)[2], const bf16x8_t (&kt)[8],
                                                 const bf16x8_t (&vt)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
     const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
+    const bf16x8_t ones = bias_ones();
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        f32x4_t Lv[4], Dv[4];
-        load_rowstats<RAGGED>(Lv, Dv, Lh, Dh, q0, qb, N, h);
-        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+        bf16x8_t bS, bD;
+        bias_operands<RAGGED>(st[qb], q0 + 32 * qb + n, N, h, fac, bS, bD);
+        f32x16_t S = mfma(bS, ones, f32x16_t{}), dP = mfma(bD, ones, f32x16_t{});
         const int row = 32 * qb + n;
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
@@ -123,7 +136,7 @@ __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, i
         uint32_t pk[8], dk[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            pds_pair<true>(S, dP, Lv, Dv, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
+            pds_pair<true>(S, dP, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int slab = ((2 * qb + hh) * 4 + s) * SLAB + l * 16;
@@ -141,7 +154,7 @@ __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, i
 // sharing the SIMD.
 template <bool RAGGED>
 __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pbuf, int q0, int N,
-                                           int key, float sc, const float* Lh, const float* Dh,
+                                           float sc, float fac, const float (&st)[2],
                                            const bf16x8_t (&kt)[8], const bf16x8_t (&vt)[8],
                                            int s, int l) {
     const int h = l >> 5, n = l & 31;
@@ -149,9 +162,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
     const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
-
-    f32x4_t Lv0[4], Dv0[4], Lv1[4], Dv1[4];
-    load_rowstats<RAGGED>(Lv0, Dv0, Lh, Dh, q0, 0, N, h);
+    const bf16x8_t ones = bias_ones();
 
     // operand of step i (i = 0..15: block i / 8, d-chunk i % 8)
     auto opoff = [&](int i) { return tile_off(32 * (i >> 3) + n, 32 * (i & 7) + 16 * h); };
@@ -161,7 +172,12 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
     aq[1] = lds_b128(sQ + opoff(1));
     ag[1] = lds_b128(sdO + opoff(1));
 
-    f32x16_t S0 = f32x16_t{}, dP0 = f32x16_t{}, S1 = f32x16_t{}, dP1 = f32x16_t{};
+    bf16x8_t bS, bD;
+    bias_operands<RAGGED>(st[0], q0 + n, N, h, fac, bS, bD);
+    f32x16_t S0 = mfma(bS, ones, f32x16_t{}), dP0 = mfma(bD, ones, f32x16_t{});
+    bias_operands<RAGGED>(st[1], q0 + 32 + n, N, h, fac, bS, bD);
+    f32x16_t S1 = mfma(bS, ones, f32x16_t{}), dP1 = mfma(bD, ones, f32x16_t{});
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
@@ -171,8 +187,6 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk[8], dk[8];
-    const int qrow0 = q0 + 4 * h, qrow1 = q0 + 32 + 4 * h;
-    load_rowstats<RAGGED>(Lv1, Dv1, Lh, Dh, q0, 1, N, h);
 #pragma unroll
     for (int i = 8; i < 16; ++i) {
         if (i + 2 < 16) {
@@ -181,7 +195,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         }
         S1 = mfma(aq[i % 3], kt[i - 8], S1);
         dP1 = mfma(ag[i % 3], vt[i - 8], dP1);
-        pds_pair<false>(S0, dP0, Lv0, Dv0, 2 * (i - 8), sc, key, qrow0, pk[i - 8], dk[i - 8]);
+        pds_pair<false>(S0, dP0, 2 * (i - 8), sc, 0, 0, pk[i - 8], dk[i - 8]);
         __builtin_amdgcn_sched_barrier(0);
     }
     // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
@@ -192,8 +206,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        pds_pair<false>(S1, dP1, Lv1, Dv1, 2 * j, sc, key, qrow1, pk[j], dk[j]);
+    for (int j = 0; j < 8; ++j) pds_pair<false>(S1, dP1, 2 * j, sc, 0, 0, pk[j], dk[j]);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int slab = ((2 + hh) * 4 + s) * SLAB + l * 16;
@@ -202,7 +215,9 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
     }
 }
 
-// Gradient role: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 rows of d.
+// Gradient role: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 rows of
+// d; the next 16-query step's operands are read while the current step's
+// products issue.
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf,
                                           f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int g,
                                           int l) {
@@ -212,18 +227,29 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
     const unsigned char* sP = smem + OFF_P + pbuf * PDS;
     const unsigned char* sS = smem + OFF_DS + pbuf * PDS;
     const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    bf16x8_t aO[2], aQ[2], bP[2][4], bS[2][4];
+    auto fetch = [&](int t, int slot) {
         const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
         const int o0 = tile_off(r0, colb), o1 = tile_off(r0 + 8, colb);
-        const bf16x8_t aO = tr16_pair(sdO + o0, sdO + o1);
-        const bf16x8_t aQ = tr16_pair(sQ + o0, sQ + o1);
+        aO[slot] = tr16_pair(sdO + o0, sdO + o1);
+        aQ[slot] = tr16_pair(sQ + o0, sQ + o1);
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
             const int slab = (t * 4 + kg) * SLAB + l * 16;
-            accdV[kg] = mfma(aO, lds_b128(sP + slab), accdV[kg]);
-            accdK[kg] = mfma(aQ, lds_b128(sS + slab), accdK[kg]);
+            bP[slot][kg] = lds_b128(sP + slab);
+            bS[slot][kg] = lds_b128(sS + slab);
         }
+    };
+    fetch(0, 0);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+            accdV[kg] = mfma(aO[t & 1], bP[t & 1][kg], accdV[kg]);
+            accdK[kg] = mfma(aQ[t & 1], bS[t & 1][kg], accdK[kg]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -271,28 +297,45 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
             kt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
             vt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
         }
-        // diagonal tiles (causal only) in a loop of their own, then the rest
+        // row statistics of tile p in st, of tile p + 1 fetched during step p
+        const float* stat = h ? Dh : Lh;
+        const float fac = h ? -1.f : -1.f / scale;
+        float st[2], nx[2];
+        st[0] = fetch_stat(stat, q_begin + n, N);
+        st[1] = fetch_stat(stat, q_begin + 32 + n, N);
+        // diagonal tiles (causal only) in a loop of their own, then the rest;
+        // the waits before each barrier cover only LDS traffic, so the next
+        // tile's statistics stay in flight across it
         int p = 0;
         for (; p < min(nmask, ntiles); ++p) {
             const int q0 = q_begin + p * BR;
+            nx[0] = fetch_stat(stat, q0 + BR + n, N);
+            nx[1] = fetch_stat(stat, q0 + BR + 32 + n, N);
             if (q0 + BR > N)
-                score_step_diag<true>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+                score_step_diag<true>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
             else
-                score_step_diag<false>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
-            __builtin_amdgcn_s_waitcnt(0);
+                score_step_diag<false>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
+            st[0] = nx[0];
+            st[1] = nx[1];
+            __builtin_amdgcn_s_waitcnt(kLgkmOnly);
             __syncthreads();
         }
         for (; p <= ntiles; ++p) {
             if (p < ntiles) {
                 const int q0 = q_begin + p * BR;
+                nx[0] = fetch_stat(stat, q0 + BR + n, N);
+                nx[1] = fetch_stat(stat, q0 + BR + 32 + n, N);
                 if (q0 + BR > N)
-                    score_step<true>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+                    score_step<true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, r4, l);
                 else
-                    score_step<false>(smem, p % 3, p & 1, q0, N, key, sc, Lh, Dh, kt, vt, r4, l);
+                    score_step<false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, r4, l);
+                st[0] = nx[0];
+                st[1] = nx[1];
             }
-            __builtin_amdgcn_s_waitcnt(0);
+            __builtin_amdgcn_s_waitcnt(kLgkmOnly);
             __syncthreads();
         }
+        __builtin_amdgcn_s_waitcnt(0);
         return;
     }
 
@@ -302,8 +345,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     for (int p = 0; p <= ntiles; ++p) {
         if (p + 1 < ntiles) {
             const int b = (p + 1) % 3;
-            stage_rows<BR, NWAVE / 2>(smem + OFF_Q + b * TILE, Qh, q_begin + (p + 1) * BR, N, r4, l);
-            stage_rows<BR, NWAVE / 2>(smem + OFF_DO + b * TILE, dOh, q_begin + (p + 1) * BR, N, r4, l);
+            stage_rows<BR, NWAVE / 2, true>(smem + OFF_Q + b * TILE, Qh, q_begin + (p + 1) * BR, N, r4, l);
+            stage_rows<BR, NWAVE / 2, true>(smem + OFF_DO + b * TILE, dOh, q_begin + (p + 1) * BR, N, r4, l);
         }
         if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, r4, l);
         __builtin_amdgcn_s_waitcnt(0);

@@ -48,8 +48,31 @@ constexpr int OFF_V = 3 * TILE;          // 2 buffers
 constexpr int OFF_DS = 5 * TILE;         // 2 buffers
 constexpr int LDS_BYTES = OFF_DS + 2 * DSB;
 
-// Score role: dS of key block k0 for this wave's 32 queries.  MASK applies
+// dS of accumulator elements r, r + 1 as one packed bf16 pair.  MASK applies
 // key > query (causal) and key >= N element by element.
+template <bool MASK, bool CAUSAL>
+__device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
+                                            float Lq, float Dq, int krow, int q, int N) {
+    float d[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int e = r + u;
+        float x = __builtin_fmaf(S[e], sc, -Lq);
+        if (MASK) {
+            const int key = krow + 8 * (e >> 2) + (e & 3);
+            if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
+        }
+        d[u] = __builtin_amdgcn_exp2f(x) * (dP[e] - Dq);
+    }
+    return pack_bf16x2(d[0], d[1]);
+}
+
+// Score role: dS of key block k0 for this wave's 32 queries, stored as slabs
+// (t = 2 mb + hh, query group s), lane-ordered 16 bytes.  Operand reads run
+// two MFMA pairs ahead; outside masked blocks the S^T/dP^T products of key
+// half 1 are interleaved with the dS arithmetic of half 0 (order pinned with
+// sched_barrier).  Masked blocks (at most two per workgroup) keep the plain
+// order, which needs fewer registers.
 template <bool MASK, bool CAUSAL>
 __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vbuf, int dbuf,
                                            int k0, int q, int N, float sc, float Lq, float Dq,
@@ -59,48 +82,87 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
     const unsigned char* sV = smem + OFF_V + vbuf * TILE;
     unsigned char* sS = smem + OFF_DS + dbuf * DSB;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        f32x16_t S = f32x16_t{}, dP = f32x16_t{};
-        const int row = 32 * mb + n;
-#pragma unroll
-        for (int dk = 0; dk < 8; ++dk) {
-            const int off = tile_off(row, 32 * dk + 16 * h);
-            S = mfma(lds_b128(sK + off), qt[dk], S);
-            dP = mfma(lds_b128(sV + off), gt[dk], dP);
-        }
-        float ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = __builtin_fmaf(S[r], sc, -Lq);
-            if (MASK) {
-                const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
-            }
-            ds[r] = __builtin_amdgcn_exp2f(x) * (dP[r] - Dq);
-        }
-        // slab (t = 2 mb + hh, query group s), lane-ordered 16 bytes
+    auto store = [&](int mb, const uint32_t (&pk)[8]) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
             *reinterpret_cast<uint4*>(sS + ((2 * mb + hh) * 4 + s) * SLAB + l * 16) =
-                pack8(ds + 8 * hh);
+                make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
+    };
+    if (MASK) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            f32x16_t S = f32x16_t{}, dP = f32x16_t{};
+            const int row = 32 * mb + n;
+#pragma unroll
+            for (int dk = 0; dk < 8; ++dk) {
+                const int off = tile_off(row, 32 * dk + 16 * h);
+                S = mfma(lds_b128(sK + off), qt[dk], S);
+                dP = mfma(lds_b128(sV + off), gt[dk], dP);
+            }
+            uint32_t pk[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                pk[j] = ds_pair<MASK, CAUSAL>(S, dP, 2 * j, sc, Lq, Dq, k0 + 32 * mb + 4 * h, q, N);
+            store(mb, pk);
+        }
+        return;
     }
+    // operand of step i (i = 0..15: key half i / 8, d-chunk i % 8)
+    auto opoff = [&](int i) { return tile_off(32 * (i >> 3) + n, 32 * (i & 7) + 16 * h); };
+    bf16x8_t ak[3], av[3];
+    ak[0] = lds_b128(sK + opoff(0));
+    av[0] = lds_b128(sV + opoff(0));
+    ak[1] = lds_b128(sK + opoff(1));
+    av[1] = lds_b128(sV + opoff(1));
+    f32x16_t S0 = f32x16_t{}, dP0 = f32x16_t{}, S1 = f32x16_t{}, dP1 = f32x16_t{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ak[(i + 2) % 3] = lds_b128(sK + opoff(i + 2));
+        av[(i + 2) % 3] = lds_b128(sV + opoff(i + 2));
+        S0 = mfma(ak[i % 3], qt[i], S0);
+        dP0 = mfma(av[i % 3], gt[i], dP0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t pk[8];
+#pragma unroll
+    for (int i = 8; i < 16; ++i) {
+        if (i + 2 < 16) {
+            ak[(i + 2) % 3] = lds_b128(sK + opoff(i + 2));
+            av[(i + 2) % 3] = lds_b128(sV + opoff(i + 2));
+        }
+        S1 = mfma(ak[i % 3], qt[i - 8], S1);
+        dP1 = mfma(av[i % 3], gt[i - 8], dP1);
+        pk[i - 8] = ds_pair<false, CAUSAL>(S0, dP0, 2 * (i - 8), sc, Lq, Dq, 0, q, N);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store(0, pk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pk[j] = ds_pair<false, CAUSAL>(S1, dP1, 2 * j, sc, Lq, Dq, 0, q, N);
+    store(1, pk);
 }
 
-// Gradient role: dQ[:, 32 g .. 32 g + 31] += dS K for the block's 64 keys.
+// Gradient role: dQ[:, 32 g .. 32 g + 31] += dS K for the block's 64 keys;
+// the next step's operands are read while the current step's products issue.
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, int dbuf,
                                           f32x16_t (&acc)[4], int g, int l) {
     const int h = l >> 5, g2 = (l >> 4) & 1;
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
     const unsigned char* sS = smem + OFF_DS + dbuf * DSB;
     const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
+    bf16x8_t bK[2], aS[2][4];
+    auto fetch = [&](int t, int slot) {
+        const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
+        bK[slot] = tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb));
+#pragma unroll
+        for (int qg = 0; qg < 4; ++qg) aS[slot][qg] = lds_b128(sS + (t * 4 + qg) * SLAB + l * 16);
+    };
+    fetch(0, 0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
-        const bf16x8_t bK = tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb));
+        if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
 #pragma unroll
-        for (int qg = 0; qg < 4; ++qg)
-            acc[qg] = mfma(lds_b128(sS + (t * 4 + qg) * SLAB + l * 16), bK, acc[qg]);
+        for (int qg = 0; qg < 4; ++qg) acc[qg] = mfma(aS[t & 1][qg], bK[t & 1], acc[qg]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
@@ -168,8 +230,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
     for (int p = 0; p <= nblk; ++p) {
         if (p + 1 < nblk) {
-            stage_rows<BK, NWAVE / 2>(smem + OFF_K + ((p + 1) % 3) * TILE, Kh, (p + 1) * BK, N, r4, l);
-            stage_rows<BK, NWAVE / 2>(smem + OFF_V + ((p + 1) & 1) * TILE, Vh, (p + 1) * BK, N, r4, l);
+            stage_rows<BK, NWAVE / 2, true>(smem + OFF_K + ((p + 1) % 3) * TILE, Kh, (p + 1) * BK, N, r4, l);
+            stage_rows<BK, NWAVE / 2, true>(smem + OFF_V + ((p + 1) & 1) * TILE, Vh, (p + 1) * BK, N, r4, l);
         }
         if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, acc, r4, l);
         __builtin_amdgcn_s_waitcnt(0);

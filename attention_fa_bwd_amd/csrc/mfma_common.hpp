@@ -32,6 +32,9 @@ typedef short i16x8_t __attribute__((ext_vector_type(8)));
 #define FA_LDS(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 constexpr float kLog2e = 1.4426950408889634f;
+// s_waitcnt operand that waits for LDS (and scalar) traffic only: vmcnt and
+// expcnt at their maxima, lgkmcnt 0.
+constexpr int kLgkmOnly = 0xC07F;
 constexpr int D = 128;       // head dim of the matrix-core kernels
 constexpr int ROWB = D * 2;  // bytes per bf16 row of Q, K, V, dO
 
@@ -66,12 +69,28 @@ __device__ __forceinline__ int tile_off(int row, int colb) {
     return row * ROWB + ((((colb >> 4) ^ swz(row)) << 4) | (colb & 15));
 }
 
+// One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes at src land at
+// LDS byte lds + 16 i.  Issued as inline assembly on purpose: for the builtin
+// form the compiler cannot tell which LDS bytes the copy writes, so it makes
+// the wave's next LDS read wait for every outstanding copy -- which would put
+// the full load latency of the next tile in front of the current tile's work.
+// Callers order these copies themselves: s_waitcnt vmcnt(0) and a barrier
+// before any wave reads the destination.  (M0 must be written one instruction
+// ahead of its use by the copy.)
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds)
+                 : "memory", "m0");
+}
+
 // Copy rows [r0, r0 + nrows) of a [N, 128] bf16 matrix into a swizzled LDS
 // tile with direct-to-LDS loads: each wave moves 1 KiB (64 lanes x 16 bytes)
 // per instruction, lane i landing at byte 16 i of the wave's slice, so lane i
 // fetches the logical chunk that the swizzle places there.  Rows at or beyond
 // N are clamped to row N - 1 (finite data; callers make them contribute 0).
-template <int NROWS, int NWAVES>
+// UNTRACKED: issue through lds_copy16 (the caller waits before use).
+template <int NROWS, int NWAVES, bool UNTRACKED = false>
 __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t* src, int r0,
                                            int N, int wave, int lane) {
     constexpr int BYTES = NROWS * ROWB;
@@ -84,9 +103,13 @@ __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t
         const int chunk = ((p % ROWB) >> 4) ^ swz(row);
         int g = r0 + row;
         g = g < N ? g : N - 1;
-        __builtin_amdgcn_global_load_lds(src + (long long)g * D + chunk * 8,
-                                         FA_LDS(void, lds_tile + wave * PER_WAVE + j * 1024), 16, 0,
-                                         0);
+        const bf16_t* gp = src + (long long)g * D + chunk * 8;
+        unsigned char* lp = lds_tile + wave * PER_WAVE + j * 1024;
+        if (UNTRACKED)
+            lds_copy16(gp, __builtin_amdgcn_readfirstlane(
+                               (uint32_t)(uintptr_t)FA_LDS(unsigned char, lp)));
+        else
+            __builtin_amdgcn_global_load_lds(gp, FA_LDS(void, lp), 16, 0, 0);
     }
 }
 
