@@ -156,16 +156,17 @@ template <bool RAGGED>
 __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pbuf, int q0, int N,
                                            float sc, float fac, const float (&st)[2],
                                            const bf16x8_t (&kt)[8], const bf16x8_t (&vt)[8],
-                                           int s, int l) {
+                                           const int (&so)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
-    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
+    const unsigned char* sdO = sQ + (OFF_DO - OFF_Q);
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
     const bf16x8_t ones = bias_ones();
 
-    // operand of step i (i = 0..15: block i / 8, d-chunk i % 8)
-    auto opoff = [&](int i) { return tile_off(32 * (i >> 3) + n, 32 * (i & 7) + 16 * h); };
+    // operand of step i (i = 0..15: block i / 8, d-chunk i % 8); rows 32 + n
+    // share row n's swizzle
+    auto opoff = [&](int i) { return so[i & 7] + 32 * ROWB * (i >> 3); };
     bf16x8_t aq[3], ag[3];
     aq[0] = lds_b128(sQ + opoff(0));
     ag[0] = lds_b128(sdO + opoff(0));
@@ -217,27 +218,24 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
 
 // Gradient role: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 rows of
 // d; the next 16-query step's operands are read while the current step's
-// products issue.
+// products issue.  ob0 / ob1: the lane's transposing-read offsets for rows
+// 4 h + (l % 16) / 4 and that + 8 (rows 16 t + ... share their swizzle).
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf,
-                                          f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int g,
-                                          int l) {
-    const int h = l >> 5, g2 = (l >> 4) & 1;
+                                          f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int ob0,
+                                          int ob1, int l) {
     const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
-    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
-    const unsigned char* sP = smem + OFF_P + pbuf * PDS;
-    const unsigned char* sS = smem + OFF_DS + pbuf * PDS;
-    const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
+    const unsigned char* q0p = sQ + ob0;
+    const unsigned char* q1p = sQ + ob1;
+    const unsigned char* sl = smem + OFF_P + pbuf * PDS + l * 16;
+    constexpr int DOQ = OFF_DO - OFF_Q, DSP = OFF_DS - OFF_P;
     bf16x8_t aO[2], aQ[2], bP[2][4], bS[2][4];
     auto fetch = [&](int t, int slot) {
-        const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
-        const int o0 = tile_off(r0, colb), o1 = tile_off(r0 + 8, colb);
-        aO[slot] = tr16_pair(sdO + o0, sdO + o1);
-        aQ[slot] = tr16_pair(sQ + o0, sQ + o1);
+        aO[slot] = tr16_pair(q0p + DOQ + 16 * ROWB * t, q1p + DOQ + 16 * ROWB * t);
+        aQ[slot] = tr16_pair(q0p + 16 * ROWB * t, q1p + 16 * ROWB * t);
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
-            const int slab = (t * 4 + kg) * SLAB + l * 16;
-            bP[slot][kg] = lds_b128(sP + slab);
-            bS[slot][kg] = lds_b128(sS + slab);
+            bP[slot][kg] = lds_b128(sl + (t * 4 + kg) * SLAB);
+            bS[slot][kg] = lds_b128(sl + DSP + (t * 4 + kg) * SLAB);
         }
     };
     fetch(0, 0);
@@ -299,18 +297,30 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
         }
         // row statistics of tile p in st, of tile p + 1 fetched during step p
         const float* stat = h ? Dh : Lh;
+        const float* statn = stat + n;
         const float fac = h ? -1.f : -1.f / scale;
+        // rows qn + n and qn + 32 + n, clamped into [0, N)
+        auto fetch2 = [&](int qn, float (&o)[2]) {
+            if (qn + BR <= N) {
+                o[0] = statn[qn];
+                o[1] = statn[qn + 32];
+            } else {
+                o[0] = fetch_stat(stat, qn + n, N);
+                o[1] = fetch_stat(stat, qn + 32 + n, N);
+            }
+        };
+        int so[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
         float st[2], nx[2];
-        st[0] = fetch_stat(stat, q_begin + n, N);
-        st[1] = fetch_stat(stat, q_begin + 32 + n, N);
+        fetch2(q_begin, st);
         // diagonal tiles (causal only) in a loop of their own, then the rest;
         // the waits before each barrier cover only LDS traffic, so the next
         // tile's statistics stay in flight across it
         int p = 0;
         for (; p < min(nmask, ntiles); ++p) {
             const int q0 = q_begin + p * BR;
-            nx[0] = fetch_stat(stat, q0 + BR + n, N);
-            nx[1] = fetch_stat(stat, q0 + BR + 32 + n, N);
+            fetch2(q0 + BR, nx);
             if (q0 + BR > N)
                 score_step_diag<true>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
             else
@@ -323,12 +333,11 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
         for (; p <= ntiles; ++p) {
             if (p < ntiles) {
                 const int q0 = q_begin + p * BR;
-                nx[0] = fetch_stat(stat, q0 + BR + n, N);
-                nx[1] = fetch_stat(stat, q0 + BR + 32 + n, N);
+                fetch2(q0 + BR, nx);
                 if (q0 + BR > N)
-                    score_step<true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, r4, l);
+                    score_step<true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
                 else
-                    score_step<false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, r4, l);
+                    score_step<false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
                 st[0] = nx[0];
                 st[1] = nx[1];
             }
@@ -342,13 +351,23 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     f32x16_t accdV[4], accdK[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) accdV[i] = accdK[i] = f32x16_t{};
+    const TileCopier<BR, NWAVE / 2> cp(r4, l);
+    const uint32_t lds0 = lds_addr(smem);
+    const int g2 = (l >> 4) & 1, colb = 64 * r4 + 32 * g2 + 8 * (l & 3);
+    const int x = 4 * h + ((l & 15) >> 2);
+    const int ob0 = tile_off(x, colb), ob1 = tile_off(x + 8, colb);
     for (int p = 0; p <= ntiles; ++p) {
+        // copies of tile p + 1 first: they need the whole phase to land
         if (p + 1 < ntiles) {
-            const int b = (p + 1) % 3;
-            stage_rows<BR, NWAVE / 2, true>(smem + OFF_Q + b * TILE, Qh, q_begin + (p + 1) * BR, N, r4, l);
-            stage_rows<BR, NWAVE / 2, true>(smem + OFF_DO + b * TILE, dOh, q_begin + (p + 1) * BR, N, r4, l);
+            const int qn = q_begin + (p + 1) * BR;
+            const uint32_t lq = lds0 + OFF_Q + ((p + 1) % 3) * TILE;
+#pragma unroll
+            for (int j = 0; j < cp.SLICES; ++j) {
+                cp.copy(j, Qh, qn, N, lq);
+                cp.copy(j, dOh, qn, N, lq + (OFF_DO - OFF_Q));
+            }
         }
-        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, r4, l);
+        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, ob0, ob1, l);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }

@@ -43,10 +43,13 @@ constexpr int NWAVE = 8;
 constexpr int TILE = BK * ROWB;          // 16 KiB
 constexpr int SLAB = 1024;               // one 32-query x 16-key bf16 operand, lane order
 constexpr int DSB = 4 * 4 * SLAB;        // dS of one block: 16 KiB
-constexpr int OFF_K = 0;                 // 3 buffers
-constexpr int OFF_V = 3 * TILE;          // 2 buffers
-constexpr int OFF_DS = 5 * TILE;         // 2 buffers
+constexpr int NKB = 4;                   // K buffers: blocks p - 1 .. p + 2
+constexpr int NVB = 3;                   // V buffers: blocks p .. p + 2
+constexpr int OFF_K = 0;
+constexpr int OFF_V = NKB * TILE;
+constexpr int OFF_DS = OFF_V + NVB * TILE;  // 2 buffers
 constexpr int LDS_BYTES = OFF_DS + 2 * DSB;
+static_assert(LDS_BYTES == 144 * 1024, "LDS plan");
 
 // dS of accumulator elements r, r + 1 as one packed bf16 pair.  MASK applies
 // key > query (causal) and key >= N element by element.
@@ -77,7 +80,7 @@ template <bool MASK, bool CAUSAL>
 __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vbuf, int dbuf,
                                            int k0, int q, int N, float sc, float Lq, float Dq,
                                            const bf16x8_t (&qt)[8], const bf16x8_t (&gt)[8],
-                                           int s, int l) {
+                                           const int (&so)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
     const unsigned char* sV = smem + OFF_V + vbuf * TILE;
@@ -107,8 +110,9 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
         }
         return;
     }
-    // operand of step i (i = 0..15: key half i / 8, d-chunk i % 8)
-    auto opoff = [&](int i) { return tile_off(32 * (i >> 3) + n, 32 * (i & 7) + 16 * h); };
+    // operand of step i (i = 0..15: key half i / 8, d-chunk i % 8); rows
+    // 32 + n share row n's swizzle
+    auto opoff = [&](int i) { return so[i & 7] + 32 * ROWB * (i >> 3); };
     bf16x8_t ak[3], av[3];
     ak[0] = lds_b128(sK + opoff(0));
     av[0] = lds_b128(sV + opoff(0));
@@ -143,18 +147,23 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
 
 // Gradient role: dQ[:, 32 g .. 32 g + 31] += dS K for the block's 64 keys;
 // the next step's operands are read while the current step's products issue.
+// ob0 / ob1: the lane's transposing-read offsets for rows 4 h + (l % 16) / 4
+// and that + 8 (rows 16 t + ... share their swizzle).  stage(t) issues part
+// of a later block's copies after step t's products, so that the copies never
+// pile up in the memory pipeline in front of this wave's work.
+template <typename Stage>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, int dbuf,
-                                          f32x16_t (&acc)[4], int g, int l) {
-    const int h = l >> 5, g2 = (l >> 4) & 1;
+                                          f32x16_t (&acc)[4], int ob0, int ob1, int l,
+                                          Stage&& stage) {
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
-    const unsigned char* sS = smem + OFF_DS + dbuf * DSB;
-    const int colb = 64 * g + 32 * g2 + 8 * (l & 3);
+    const unsigned char* k0p = sK + ob0;
+    const unsigned char* k1p = sK + ob1;
+    const unsigned char* sl = smem + OFF_DS + dbuf * DSB + l * 16;
     bf16x8_t bK[2], aS[2][4];
     auto fetch = [&](int t, int slot) {
-        const int r0 = 16 * t + 4 * h + ((l & 15) >> 2);
-        bK[slot] = tr16_pair(sK + tile_off(r0, colb), sK + tile_off(r0 + 8, colb));
+        bK[slot] = tr16_pair(k0p + 16 * ROWB * t, k1p + 16 * ROWB * t);
 #pragma unroll
-        for (int qg = 0; qg < 4; ++qg) aS[slot][qg] = lds_b128(sS + (t * 4 + qg) * SLAB + l * 16);
+        for (int qg = 0; qg < 4; ++qg) aS[slot][qg] = lds_b128(sl + (t * 4 + qg) * SLAB);
     };
     fetch(0, 0);
 #pragma unroll
@@ -162,6 +171,7 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
         if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
 #pragma unroll
         for (int qg = 0; qg < 4; ++qg) acc[qg] = mfma(aS[t & 1][qg], bK[t & 1], acc[qg]);
+        stage(t);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -191,13 +201,18 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     const int full = CAUSAL ? min(q0 / BK, N / BK) : N / BK;  // blocks needing no mask
     const float sc = scale * kLog2e;
 
+    // blocks 0 and 1 up front; block p + 2 is copied during phase p
     stage_rows<BK, NWAVE>(smem + OFF_K, Kh, 0, N, wave, l);
     stage_rows<BK, NWAVE>(smem + OFF_V, Vh, 0, N, wave, l);
+    if (nblk > 1) {
+        stage_rows<BK, NWAVE>(smem + OFF_K + TILE, Kh, BK, N, wave, l);
+        stage_rows<BK, NWAVE>(smem + OFF_V + TILE, Vh, BK, N, wave, l);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // Phase p (one barrier each, nblk + 1 phases): score waves work on block p;
-    // gradient waves stage block p + 1 and work on block p - 1 (the score
+    // gradient waves copy block p + 2 and work on block p - 1 (the score
     // waves' MFMA work is twice theirs).  Each role has its own loop so their
     // registers never coexist.
     if (score) {
@@ -210,14 +225,17 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         }
         const float Lq = Lg[(long long)head * N + qc] * kLog2e;
         const float Dq = Dg[(long long)head * N + qc];
+        int so[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
         for (int p = 0; p <= nblk; ++p) {
             if (p < nblk) {
                 if (p < full)
-                    score_step<false, CAUSAL>(smem, p % 3, p & 1, p & 1, p * BK, q, N, sc, Lq, Dq,
-                                              qt, gt, r4, l);
+                    score_step<false, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
+                                              Dq, qt, gt, so, r4, l);
                 else
-                    score_step<true, CAUSAL>(smem, p % 3, p & 1, p & 1, p * BK, q, N, sc, Lq, Dq,
-                                             qt, gt, r4, l);
+                    score_step<true, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
+                                             Dq, qt, gt, so, r4, l);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -228,13 +246,35 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     f32x16_t acc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    const TileCopier<BK, NWAVE / 2> cp(r4, l);
+    const uint32_t lds0 = lds_addr(smem);
+    const int g2 = (l >> 4) & 1, colb = 64 * r4 + 32 * g2 + 8 * (l & 3);
+    const int x = 4 * h + ((l & 15) >> 2);
+    const int ob0 = tile_off(x, colb), ob1 = tile_off(x + 8, colb);
     for (int p = 0; p <= nblk; ++p) {
-        if (p + 1 < nblk) {
-            stage_rows<BK, NWAVE / 2, true>(smem + OFF_K + ((p + 1) % 3) * TILE, Kh, (p + 1) * BK, N, r4, l);
-            stage_rows<BK, NWAVE / 2, true>(smem + OFF_V + ((p + 1) & 1) * TILE, Vh, (p + 1) * BK, N, r4, l);
+        // copies of block p + 2 first; block p + 1's (issued one phase ago)
+        // must have landed by the barrier, these may stay in flight
+        const bool more = p + 2 < nblk;
+        const int kn = (p + 2) * BK;
+        const uint32_t lk = lds0 + OFF_K + ((p + 2) % NKB) * TILE;
+        const uint32_t lv = lds0 + OFF_V + ((p + 2) % NVB) * TILE;
+        auto stage = [&](int j) {
+            if (more) {
+                cp.copy(j, Kh, kn, N, lk);
+                cp.copy(j, Vh, kn, N, lv);
+            }
+        };
+        static_assert(TileCopier<BK, NWAVE / 2>::SLICES == 4, "one slice per 16-key step");
+        if (p >= 1) {
+            grad_step(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, l, stage);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stage(j);
         }
-        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, acc, r4, l);
-        __builtin_amdgcn_s_waitcnt(0);
+        if (more)
+            __builtin_amdgcn_s_waitcnt(kVmcnt8Lgkm0);
+        else
+            __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 

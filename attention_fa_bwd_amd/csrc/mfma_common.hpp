@@ -35,6 +35,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // s_waitcnt operand that waits for LDS (and scalar) traffic only: vmcnt and
 // expcnt at their maxima, lgkmcnt 0.
 constexpr int kLgkmOnly = 0xC07F;
+// s_waitcnt operand: at most 8 vector-memory operations outstanding, LDS and
+// scalar traffic drained (vmcnt 8, expcnt 7, lgkmcnt 0).
+constexpr int kVmcnt8Lgkm0 = 0x0078;
 constexpr int D = 128;       // head dim of the matrix-core kernels
 constexpr int ROWB = D * 2;  // bytes per bf16 row of Q, K, V, dO
 
@@ -76,13 +79,18 @@ __device__ __forceinline__ int tile_off(int row, int colb) {
 // the full load latency of the next tile in front of the current tile's work.
 // Callers order these copies themselves: s_waitcnt vmcnt(0) and a barrier
 // before any wave reads the destination.  (M0 must be written one instruction
-// ahead of its use by the copy.)
+// ahead of its use by the copy.  The compiler reserves M0 and sets it right
+// before each of its own uses, so overwriting it here is safe; it warns about
+// the clobber all the same.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(src), "s"(lds)
                  : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Copy rows [r0, r0 + nrows) of a [N, 128] bf16 matrix into a swizzled LDS
 // tile with direct-to-LDS loads: each wave moves 1 KiB (64 lanes x 16 bytes)
@@ -111,6 +119,66 @@ __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t
         else
             __builtin_amdgcn_global_load_lds(gp, FA_LDS(void, lp), 16, 0, 0);
     }
+}
+
+// The same copy with a scalar base address and a 32-bit per-lane offset.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16_sbase(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(base), "s"(lds)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Copies NROWS-row tiles of [N, 128] bf16 matrices into swizzled LDS tiles
+// with NWAVES waves, one 1 KiB slice (one direct-to-LDS copy) at a time, so
+// that the copies of a tile can be spread over the work of a loop iteration.
+// The per-lane byte offsets of the slices are computed once; a full tile then
+// needs only scalar address arithmetic per copy.  Rows at or beyond N (a
+// ragged last tile) are clamped to row N - 1.  Callers wait (vmcnt(0)) and
+// synchronise before any wave reads the tile.
+template <int NROWS, int NWAVES>
+struct TileCopier {
+    static constexpr int PER_WAVE = NROWS * ROWB / NWAVES;
+    static constexpr int SLICES = PER_WAVE / 1024;
+    static_assert(PER_WAVE % 1024 == 0, "tile must split into 1 KiB slices per wave");
+    uint32_t voff[SLICES];  // byte offset of this lane's 16 bytes within the tile's rows
+    uint32_t lds_wave;      // LDS byte offset of this wave's first slice within a tile
+    int rowj[SLICES];       // tile row of this lane's 16 bytes, slice j
+
+    __device__ __forceinline__ TileCopier(int wave, int lane) {
+        lds_wave = (uint32_t)__builtin_amdgcn_readfirstlane(wave * PER_WAVE);
+#pragma unroll
+        for (int j = 0; j < SLICES; ++j) {
+            const int p = wave * PER_WAVE + j * 1024 + lane * 16;
+            const int row = p / ROWB;
+            const int chunk = ((p % ROWB) >> 4) ^ swz(row);
+            rowj[j] = row;
+            voff[j] = (uint32_t)(row * ROWB + chunk * 16);
+        }
+    }
+    // slice j of rows [r0, r0 + NROWS) of src into the LDS tile at byte lds_tile
+    __device__ __forceinline__ void copy(int j, const bf16_t* src, int r0, int N,
+                                         uint32_t lds_tile) const {
+        const uint32_t lds = lds_tile + lds_wave + j * 1024;
+        if (r0 + NROWS <= N) {
+            lds_copy16_sbase(src + (long long)r0 * D, voff[j], lds);
+        } else {
+            int g = r0 + rowj[j];
+            g = g < N ? g : N - 1;
+            lds_copy16(reinterpret_cast<const unsigned char*>(src + (long long)g * D) +
+                           (voff[j] & (ROWB - 1)),
+                       lds);
+        }
+    }
+};
+
+// LDS byte address of a pointer into a __shared__ array (wave-uniform).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane(
+        (int)(uintptr_t)FA_LDS(const unsigned char, p));
 }
 
 __device__ __forceinline__ uint4 pack8(const float* v) {
