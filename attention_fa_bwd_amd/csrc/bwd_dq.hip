@@ -23,9 +23,10 @@
 //     read the K operand of that block (key on the contraction index) with
 //     ds_read_b64_tr_b16 -- each fragment feeds four products, one per query
 //     group -- and dS straight from the slabs;
-//   * K blocks rotate through three LDS buffers (score waves read block p,
-//     gradient waves block p - 1, loads fill block p + 1 with direct-to-LDS
-//     copies), V blocks through two, dS through two.  One barrier per block;
+//   * K blocks rotate through four LDS buffers (score waves read block p,
+//     gradient waves block p - 1, block p + 1 has landed, direct-to-LDS
+//     copies fill block p + 2, spread over the gradient steps), V blocks
+//     through three, dS through two (144 KiB).  One barrier per block;
 //   * rows at or beyond N are staged as copies of row N - 1; in the last key
 //     block their P is forced to 0, and query rows at or beyond N are not
 //     stored.

@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -50,11 +51,16 @@ def parse():
 
 
 def kernel_source_hash() -> str:
+    """Hash of the main kernels' code with comments and blank space removed, so
+    that a comment edit does not invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for rel in MAIN_KERNEL_SOURCES + ["attention_fa_bwd_amd/csrc/common.hpp"]:
         path = os.path.join(ROOT, rel)
         if os.path.exists(path):
-            h.update(open(path, "rb").read())
+            text = open(path, encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
