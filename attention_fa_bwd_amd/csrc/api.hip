@@ -49,8 +49,12 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V, void* O, 
     int rc = check(dtype, B, H, N, d, {Q, K, V, O, L});
     if (rc != FA_OK) return rc;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_fwd(dtype, Q, K, V, O, L, fa::Shape{B, H, N, d}, scale,
-                                     causal != 0, (hipStream_t)stream));
+    const fa::Shape s{B, H, N, d};
+    if (dtype == FA_DTYPE_BF16 && d == 128)
+        return hip_status(fa::launch_fwd_d128(Q, K, V, O, L, s, scale, causal != 0,
+                                              (hipStream_t)stream));
+    return hip_status(fa::launch_fwd(dtype, Q, K, V, O, L, s, scale, causal != 0,
+                                     (hipStream_t)stream));
 }
 
 int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D, float* dq_accum,

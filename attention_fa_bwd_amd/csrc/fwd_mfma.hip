@@ -1,0 +1,241 @@
+// fwd_mfma.hip -- attention forward on gfx950 matrix cores, bf16, head dim 128:
+// O and the logsumexp L (supporting step: they feed the backward).
+//
+// Query blocks outer, key blocks inner, online softmax per query
+// (1point3acres post "手扒了FlashAttention": running max m, denominator l and
+// accumulator a; per key block the accumulator and denominator are rebased
+// to the new maximum before the block's terms are added; finally O = a / l
+// and L = m + log l, which FA2 chapter 16 sec 16.4 stores for the backward).
+// The rebase is lazy: the maximum the terms are taken against only moves
+// when the block maximum exceeds it by more than 2^8 (in exp2 units), so most
+// blocks skip rescaling the accumulator; every term stays below 2^8 and the
+// quotient a / l is unchanged.  Under the causal mask the key loop stops at
+// the diagonal (FA2 chapter 16 sec 16.8 item 2).
+//
+// gfx950 mapping: 8 waves, two per SIMD; wave w owns queries [32 w, +32) of
+// the workgroup's 256 (its Q^T B-operand fragments stay in registers).  Key
+// blocks of 64 run in phases, one barrier each; in phase j a wave forms
+// S^T = K Q^T of block j (key on rows, query on lanes: a query's maximum,
+// denominator and rescale factor are per-lane values) while, in between those
+// products, it adds O^T += V^T P^T of block j - 1: P^T straight from registers
+// (accumulator layout, contraction index permuted), V^T through
+// ds_read_b64_tr_b16.  Then it turns S^T into P^T for the next phase.  All
+// waves copy parts of key block j + 2 of K and V into LDS (direct-to-LDS
+// loads); K rotates through three buffers, V through four (112 KiB).  Key rows
+// at or beyond N are staged as copies of row N - 1 and masked; query rows at
+// or beyond N are not stored.
+#include "launch.hpp"
+#include "mfma_common.hpp"
+
+namespace fa {
+namespace {
+
+using namespace mf;
+
+constexpr int BQ = 256;                  // queries per workgroup
+constexpr int BK = 64;                   // keys per block
+constexpr int NWAVE = 8;
+constexpr int TILE = BK * ROWB;          // 16 KiB
+constexpr int SD = 2;                    // blocks copied ahead
+constexpr int NKB = SD + 1;              // K buffers: blocks j .. j + SD
+constexpr int NVB = SD + 2;              // V buffers: blocks j - 1 .. j + SD
+constexpr int OFF_K = 0;
+constexpr int OFF_V = NKB * TILE;
+constexpr int LDS_BYTES = OFF_V + NVB * TILE;
+static_assert(LDS_BYTES == 112 * 1024, "LDS plan");
+constexpr float kLazy = 8.f;             // rebase threshold, log2 units
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    bf16_t* __restrict__ O, float* __restrict__ Lg, int N, int nqb, float scale) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+
+    const int work = xcd_work_item(blockIdx.x, gridDim.x);
+    const int head = work / nqb;
+    const int qblk = CAUSAL ? nqb - 1 - work % nqb : work % nqb;  // heaviest first
+    const int q0 = qblk * BQ;
+    const long long hoff = (long long)head * N * D;
+    const bf16_t* Kh = K + hoff;
+    const bf16_t* Vh = V + hoff;
+
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
+    const int q = q0 + 32 * wave + n;  // this lane's query
+    const int kend = CAUSAL ? min(N, q0 + BQ) : N;
+    const int nblk = (kend + BK - 1) / BK;
+    const int full = CAUSAL ? min(q0 / BK, N / BK) : N / BK;  // blocks needing no mask
+    const float sc = scale * kLog2e;
+
+#pragma unroll
+    for (int b = 0; b < SD; ++b) {
+        if (b < nblk) {
+            stage_rows<BK, NWAVE>(smem + OFF_K + b * TILE, Kh, b * BK, N, wave, l);
+            stage_rows<BK, NWAVE>(smem + OFF_V + b * TILE, Vh, b * BK, N, wave, l);
+        }
+    }
+    const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
+    bf16x8_t qt[8];
+#pragma unroll
+    for (int dk = 0; dk < 8; ++dk)
+        qt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // per-lane operand offsets: S^T A operand (K row n, d-chunk i, this half);
+    // V^T A operand (transposing reads of key rows 4 h + (l % 16) / 4 and + 8,
+    // d-block db) -- key rows 32 + ... and 16 t + ... share their swizzle
+    int so[8], ob0[4], ob1[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
+    {
+        const int g2 = (l >> 4) & 1, x = 4 * h + ((l & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const int colb = 64 * db + 32 * g2 + 8 * (l & 3);
+            ob0[db] = tile_off(x, colb);
+            ob1[db] = tile_off(x + 8, colb);
+        }
+    }
+    const TileCopier<BK, NWAVE> cp(wave, l);
+    const uint32_t lds0 = lds_addr(smem);
+
+    f32x16_t acc[4];  // O^T of d-block db: lane = query, rows 32 db + 8 (r / 4) + 4 h + r % 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    bf16x8_t pb[4];   // P^T of the previous block, 16-key step t = 2 mb + hh
+    float mu = -1e30f, lsum = 0.f;
+
+    for (int j = 0; j <= nblk; ++j) {
+        const bool more = j + SD < nblk;
+        if (more) {
+            const int kn = (j + SD) * BK;
+            const uint32_t lk = lds0 + OFF_K + ((j + SD) % NKB) * TILE;
+            const uint32_t lv = lds0 + OFF_V + ((j + SD) % NVB) * TILE;
+#pragma unroll
+            for (int s = 0; s < cp.SLICES; ++s) {
+                cp.copy(s, Kh, kn, N, lk);
+                cp.copy(s, Vh, kn, N, lv);
+            }
+        }
+        const bool mf = j < nblk, pv = j >= 1;
+        const unsigned char* sK = smem + OFF_K + (j % NKB) * TILE;
+        const unsigned char* sV = smem + OFF_V + ((j + NVB - 1) % NVB) * TILE;
+        f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
+        // 16 steps: S^T product i (key half i / 8, d-chunk i % 8) and O^T product
+        // i (16-key step i / 4, d-block i % 4); operands two / one steps ahead
+        bf16x8_t ak[3], av[2];
+        auto kop = [&](int i) { return lds_b128(sK + so[i & 7] + 32 * ROWB * (i >> 3)); };
+        auto vop = [&](int i) {
+            const int t = i >> 2, db = i & 3;
+            return tr16_pair(sV + ob0[db] + 16 * ROWB * t, sV + ob1[db] + 16 * ROWB * t);
+        };
+        if (mf) {
+            ak[0] = kop(0);
+            ak[1] = kop(1);
+        }
+        if (pv) av[0] = vop(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (mf) {
+                if (i + 2 < 16) ak[(i + 2) % 3] = kop(i + 2);
+                if (i < 8)
+                    S0 = mfma(ak[i % 3], qt[i], S0);
+                else
+                    S1 = mfma(ak[i % 3], qt[i - 8], S1);
+            }
+            if (pv) {
+                if (i + 1 < 16) av[(i + 1) & 1] = vop(i + 1);
+                acc[i & 3] = mfma(av[i & 1], pb[i >> 2], acc[i & 3]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (mf) {
+            // scores in exp2 units, masked where needed
+            float s2[32];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                s2[r] = S0[r] * sc;
+                s2[16 + r] = S1[r] * sc;
+            }
+            if (j >= full) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    const int key = j * BK + 32 * (e >> 4) + 8 * ((e & 15) >> 2) + 4 * h + (e & 3);
+                    if (key >= N || (CAUSAL && key > q)) s2[e] = -INFINITY;
+                }
+            }
+            float bm = s2[0];
+#pragma unroll
+            for (int e = 1; e < 32; ++e) bm = fmaxf(bm, s2[e]);
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const bool rebase = bm > mu + kLazy;
+            if (__ballot(rebase)) {
+                const float alpha = rebase ? __builtin_amdgcn_exp2f(mu - bm) : 1.f;
+                mu = rebase ? bm : mu;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            }
+            float p[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) {
+                p[e] = __builtin_amdgcn_exp2f(s2[e] - mu);
+                lsum += p[e];
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                pb[t] = as_bf16x8(make_uint4(pack_bf16x2(p[8 * t], p[8 * t + 1]),
+                                             pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
+                                             pack_bf16x2(p[8 * t + 4], p[8 * t + 5]),
+                                             pack_bf16x2(p[8 * t + 6], p[8 * t + 7])));
+        }
+        // block j + 1's copies (issued one phase ago) must have landed; this
+        // phase's may stay in flight
+        if (more)
+            __builtin_amdgcn_s_waitcnt(kVmcnt4Lgkm0);
+        else
+            __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (q < N) {
+        const float inv = 1.f / ltot;
+        bf16_t* orow = O + hoff + (long long)q * D;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int r = 4 * a4;
+                uint2 v;
+                v.x = pack_bf16x2(acc[db][r] * inv, acc[db][r + 1] * inv);
+                v.y = pack_bf16x2(acc[db][r + 2] * inv, acc[db][r + 3] * inv);
+                *reinterpret_cast<uint2*>(orow + 32 * db + 8 * a4 + 4 * h) = v;
+            }
+        if (h == 0) Lg[(long long)head * N + q] = (mu + __builtin_log2f(ltot)) * kLn2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_d128(const void* Q, const void* K, const void* V, void* O, float* L,
+                           Shape s, float scale, bool causal, hipStream_t st) {
+    const int nqb = (s.N + BQ - 1) / BQ;
+    const long long nwork = (long long)nqb * s.H * s.B;
+    if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nwork);
+    if (causal)
+        hipLaunchKernelGGL((fwd_mfma_kernel<true>), grid, dim3(NWAVE * 64), 0, st,
+                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, L,
+                           s.N, nqb, scale);
+    else
+        hipLaunchKernelGGL((fwd_mfma_kernel<false>), grid, dim3(NWAVE * 64), 0, st,
+                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, L,
+                           s.N, nqb, scale);
+    return hipGetLastError();
+}
+
+}  // namespace fa

@@ -16,6 +16,10 @@ hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s
 hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, void* O,
                       float* L, Shape s, float scale, bool causal, hipStream_t st);
 
+// Matrix-core forward, bf16, head dim 128.
+hipError_t launch_fwd_d128(const void* Q, const void* K, const void* V, void* O, float* L,
+                           Shape s, float scale, bool causal, hipStream_t st);
+
 // Vector-ALU backward (fp32 FMA): every dtype and head dim.
 hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* V,
                            const void* dO, const float* L, const float* D, float* dq_accum,

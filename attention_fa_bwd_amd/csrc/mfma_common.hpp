@@ -38,6 +38,7 @@ constexpr int kLgkmOnly = 0xC07F;
 // s_waitcnt operand: at most 8 vector-memory operations outstanding, LDS and
 // scalar traffic drained (vmcnt 8, expcnt 7, lgkmcnt 0).
 constexpr int kVmcnt8Lgkm0 = 0x0078;
+constexpr int kVmcnt4Lgkm0 = 0x0074;
 constexpr int D = 128;       // head dim of the matrix-core kernels
 constexpr int ROWB = D * 2;  // bytes per bf16 row of Q, K, V, dO
 

@@ -63,7 +63,10 @@ typedef enum {
  * alpha = exp(m - m') at each key block), O = a / l and L = m + log l
  * (1point3acres post "手扒了FlashAttention", the online-softmax recurrence and
  * the logsumexp; FA2 chapter 16 sec 16.4).  Supporting step of the backward:
- * it provides O and L for benchmarking and end-to-end checks.
+ * it provides O and L for benchmarking and end-to-end checks.  bf16 with
+ * d = 128 runs on the matrix cores and rebases lazily (only when a block's
+ * maximum exceeds the running one by more than a factor 2^8, which leaves
+ * O and L unchanged in exact arithmetic); other cases run a vector-ALU kernel.
  *   in : Q, K, V [B,H,N,d] dtype
  *   out: O [B,H,N,d] dtype (rounded to nearest even for bf16), L [B,H,N] fp32
  */
