@@ -21,6 +21,7 @@ __all__ = [
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_F16 = 2
 FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -81,6 +82,8 @@ def _dtype_code(t: torch.Tensor) -> int:
         return FA_DTYPE_BF16
     if t.dtype == torch.float32:
         return FA_DTYPE_F32
+    if t.dtype == torch.float16:
+        return FA_DTYPE_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 

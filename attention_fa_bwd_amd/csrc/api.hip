@@ -21,7 +21,14 @@ bool dims_ok(int B, int H, int N, int d) {
     return e < (1LL << 40);
 }
 
-bool dtype_ok(int dtype) { return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16; }
+bool dtype_ok(int dtype) {
+    return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
+}
+
+// The matrix-core kernels: 16-bit elements, head dim 128.
+bool matrix_core(int dtype, int d) {
+    return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128;
+}
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
@@ -50,8 +57,8 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V, void* O, 
     if (rc != FA_OK) return rc;
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
-    if (dtype == FA_DTYPE_BF16 && d == 128)
-        return hip_status(fa::launch_fwd_d128(Q, K, V, O, L, s, scale, causal != 0,
+    if (matrix_core(dtype, d))
+        return hip_status(fa::launch_fwd_d128(dtype, Q, K, V, O, L, s, scale, causal != 0,
                                               (hipStream_t)stream));
     return hip_status(fa::launch_fwd(dtype, Q, K, V, O, L, s, scale, causal != 0,
                                      (hipStream_t)stream));
@@ -74,12 +81,12 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     const hipStream_t st = (hipStream_t)stream;
-    // one kernel per (dtype, head dim): matrix cores for bf16 d=128, vector ALUs otherwise
-    if (dtype == FA_DTYPE_BF16 && d == 128) {
-        int rc2 = hip_status(fa::launch_bwd_dq_d128(Q, K, V, dO, L, D, dq_accum, s, scale,
+    // one kernel per (dtype, head dim): matrix cores for 16-bit d=128, vector ALUs otherwise
+    if (matrix_core(dtype, d)) {
+        int rc2 = hip_status(fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, s, scale,
                                                     causal != 0, st));
         if (rc2 != FA_OK) return rc2;
-        return hip_status(fa::launch_bwd_dkdv_d128(Q, K, V, dO, L, D, dK, dV, s, scale,
+        return hip_status(fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, s, scale,
                                                    causal != 0, st));
     }
     return hip_status(fa::launch_bwd_simt(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
@@ -91,9 +98,9 @@ int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const vo
                 float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dK, dV});
     if (rc != FA_OK) return rc;
-    if (!(dtype == FA_DTYPE_BF16 && d == 128)) return FA_EUNSUPPORTED;
+    if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_bwd_dkdv_d128(Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d},
+    return hip_status(fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d},
                                                scale, causal != 0, (hipStream_t)stream));
 }
 
@@ -102,9 +109,9 @@ int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V, const void
               float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum});
     if (rc != FA_OK) return rc;
-    if (!(dtype == FA_DTYPE_BF16 && d == 128)) return FA_EUNSUPPORTED;
+    if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_bwd_dq_d128(Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d},
+    return hip_status(fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d},
                                              scale, causal != 0, (hipStream_t)stream));
 }
 

@@ -74,24 +74,24 @@ __device__ __forceinline__ float fetch_stat(const float* src, int q, int N) {
 // dP = 0.
 template <bool RAGGED>
 __device__ __forceinline__ void bias_operands(float raw, int q, int N, int h, float fac,
-                                              bf16x8_t& aS, bf16x8_t& aD) {
+                                              v16x8_t& aS, v16x8_t& aD) {
     float u = raw * fac;
     if (RAGGED && q >= N) u = h ? 0.f : -1e30f;
     const float hi = (float)(__bf16)u;
     const float r1 = u - hi;
     const float mid = (float)(__bf16)r1;
     const uint32_t w0 = pack_bf16x2(hi, mid), w1 = pack_bf16x2(r1 - mid, 0.f);
-    aS = as_bf16x8(h ? make_uint4(0, 0, 0, 0) : make_uint4(w0, w1, 0, 0));
-    aD = as_bf16x8(h ? make_uint4(w0, w1, 0, 0) : make_uint4(0, 0, 0, 0));
+    aS = as_v16x8(h ? make_uint4(0, 0, 0, 0) : make_uint4(w0, w1, 0, 0));
+    aD = as_v16x8(h ? make_uint4(w0, w1, 0, 0) : make_uint4(0, 0, 0, 0));
 }
 
 // 1.0 on k-slots 0..2 of every lane: B operand of the bias products
-__device__ __forceinline__ bf16x8_t bias_ones() {
-    return as_bf16x8(make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
+__device__ __forceinline__ v16x8_t bias_ones() {
+    return as_v16x8(make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
 }
 
 // P and dS of accumulator elements r, r + 1 (one packed bf16 pair each).
-template <bool MASK>
+template <typename E, bool MASK>
 __device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
                                          int key, int qrow, uint32_t& pp, uint32_t& pd) {
     float p[2], d[2];
@@ -103,40 +103,40 @@ __device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP, 
         p[u] = __builtin_amdgcn_exp2f(x);
         d[u] = p[u] * dP[e];
     }
-    pp = pack_bf16x2(p[0], p[1]);
-    pd = pack_bf16x2(d[0], d[1]);
+    pp = E::pack2(p[0], p[1]);
+    pd = E::pack2(d[0], d[1]);
 }
 
 // Score role on a diagonal tile (causal mask applied element by element):
 // block by block, no interleaving -- two such tiles per workgroup, and the
 // mask needs registers the interleaved order does not have to spare.
-template <bool RAGGED>
+template <typename E, bool RAGGED>
 __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, int pbuf, int q0,
                                                 int N, int key, float sc, float fac,
-                                                const float (&st)[2], const bf16x8_t (&kt)[8],
-                                                const bf16x8_t (&vt)[8], int s, int l) {
+                                                const float (&st)[2], const v16x8_t (&kt)[8],
+                                                const v16x8_t (&vt)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
     const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
-    const bf16x8_t ones = bias_ones();
+    const v16x8_t ones = bias_ones();
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-        bf16x8_t bS, bD;
+        v16x8_t bS, bD;
         bias_operands<RAGGED>(st[qb], q0 + 32 * qb + n, N, h, fac, bS, bD);
         f32x16_t S = mfma(bS, ones, f32x16_t{}), dP = mfma(bD, ones, f32x16_t{});
         const int row = 32 * qb + n;
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
             const int off = tile_off(row, 32 * dk + 16 * h);
-            S = mfma(lds_b128(sQ + off), kt[dk], S);
-            dP = mfma(lds_b128(sdO + off), vt[dk], dP);
+            S = E::mma(lds_b128(sQ + off), kt[dk], S);
+            dP = E::mma(lds_b128(sdO + off), vt[dk], dP);
         }
         uint32_t pk[8], dk[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            pds_pair<true>(S, dP, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
+            pds_pair<E, true>(S, dP, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int slab = ((2 * qb + hh) * 4 + s) * SLAB + l * 16;
@@ -152,28 +152,28 @@ __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, i
 // MFMA pairs ahead; the S/dP products of block 1 are interleaved with the P/dS
 // arithmetic of block 0; block 1's arithmetic then overlaps the gradient wave
 // sharing the SIMD.
-template <bool RAGGED>
+template <typename E, bool RAGGED>
 __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pbuf, int q0, int N,
                                            float sc, float fac, const float (&st)[2],
-                                           const bf16x8_t (&kt)[8], const bf16x8_t (&vt)[8],
+                                           const v16x8_t (&kt)[8], const v16x8_t (&vt)[8],
                                            const int (&so)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
     const unsigned char* sdO = sQ + (OFF_DO - OFF_Q);
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
-    const bf16x8_t ones = bias_ones();
+    const v16x8_t ones = bias_ones();
 
     // operand of step i (i = 0..15: block i / 8, d-chunk i % 8); rows 32 + n
     // share row n's swizzle
     auto opoff = [&](int i) { return so[i & 7] + 32 * ROWB * (i >> 3); };
-    bf16x8_t aq[3], ag[3];
+    v16x8_t aq[3], ag[3];
     aq[0] = lds_b128(sQ + opoff(0));
     ag[0] = lds_b128(sdO + opoff(0));
     aq[1] = lds_b128(sQ + opoff(1));
     ag[1] = lds_b128(sdO + opoff(1));
 
-    bf16x8_t bS, bD;
+    v16x8_t bS, bD;
     bias_operands<RAGGED>(st[0], q0 + n, N, h, fac, bS, bD);
     f32x16_t S0 = mfma(bS, ones, f32x16_t{}), dP0 = mfma(bD, ones, f32x16_t{});
     bias_operands<RAGGED>(st[1], q0 + 32 + n, N, h, fac, bS, bD);
@@ -183,8 +183,8 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
     for (int i = 0; i < 8; ++i) {
         aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
         ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
-        S0 = mfma(aq[i % 3], kt[i], S0);
-        dP0 = mfma(ag[i % 3], vt[i], dP0);
+        S0 = E::mma(aq[i % 3], kt[i], S0);
+        dP0 = E::mma(ag[i % 3], vt[i], dP0);
         __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk[8], dk[8];
@@ -194,9 +194,9 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
             aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
             ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
         }
-        S1 = mfma(aq[i % 3], kt[i - 8], S1);
-        dP1 = mfma(ag[i % 3], vt[i - 8], dP1);
-        pds_pair<false>(S0, dP0, 2 * (i - 8), sc, 0, 0, pk[i - 8], dk[i - 8]);
+        S1 = E::mma(aq[i % 3], kt[i - 8], S1);
+        dP1 = E::mma(ag[i % 3], vt[i - 8], dP1);
+        pds_pair<E, false>(S0, dP0, 2 * (i - 8), sc, 0, 0, pk[i - 8], dk[i - 8]);
         __builtin_amdgcn_sched_barrier(0);
     }
     // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
@@ -207,7 +207,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pds_pair<false>(S1, dP1, 2 * j, sc, 0, 0, pk[j], dk[j]);
+    for (int j = 0; j < 8; ++j) pds_pair<E, false>(S1, dP1, 2 * j, sc, 0, 0, pk[j], dk[j]);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int slab = ((2 + hh) * 4 + s) * SLAB + l * 16;
@@ -220,6 +220,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
 // d; the next 16-query step's operands are read while the current step's
 // products issue.  ob0 / ob1: the lane's transposing-read offsets for rows
 // 4 h + (l % 16) / 4 and that + 8 (rows 16 t + ... share their swizzle).
+template <typename E>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf,
                                           f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int ob0,
                                           int ob1, int l) {
@@ -228,7 +229,7 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
     const unsigned char* q1p = sQ + ob1;
     const unsigned char* sl = smem + OFF_P + pbuf * PDS + l * 16;
     constexpr int DOQ = OFF_DO - OFF_Q, DSP = OFF_DS - OFF_P;
-    bf16x8_t aO[2], aQ[2], bP[2][4], bS[2][4];
+    v16x8_t aO[2], aQ[2], bP[2][4], bS[2][4];
     auto fetch = [&](int t, int slot) {
         aO[slot] = tr16_pair(q0p + DOQ + 16 * ROWB * t, q1p + DOQ + 16 * ROWB * t);
         aQ[slot] = tr16_pair(q0p + 16 * ROWB * t, q1p + 16 * ROWB * t);
@@ -244,26 +245,26 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
         if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
-            accdV[kg] = mfma(aO[t & 1], bP[t & 1][kg], accdV[kg]);
-            accdK[kg] = mfma(aQ[t & 1], bS[t & 1][kg], accdK[kg]);
+            accdV[kg] = E::mma(aO[t & 1], bP[t & 1][kg], accdV[kg]);
+            accdK[kg] = E::mma(aQ[t & 1], bS[t & 1][kg], accdK[kg]);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <bool CAUSAL>
+template <typename E, bool CAUSAL>
 __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int N, int nkb, float scale) {
+    const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
+    const e16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
+    e16_t* __restrict__ dK, e16_t* __restrict__ dV, int N, int nkb, float scale) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
     const int head = work / nkb;
     const int k0 = (work % nkb) * BC;  // heaviest key blocks first under the causal mask
     const long long hoff = (long long)head * N * D;
-    const bf16_t* Qh = Q + hoff;
-    const bf16_t* dOh = dO + hoff;
+    const e16_t* Qh = Q + hoff;
+    const e16_t* dOh = dO + hoff;
     const float* Lh = Lg + (long long)head * N;
     const float* Dh = Dg + (long long)head * N;
 
@@ -289,11 +290,11 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     // coexist with the other role's.
     if (score) {
         const int keyc = key < N ? key : N - 1;  // clamped: finite data, outputs not stored
-        bf16x8_t kt[8], vt[8];
+        v16x8_t kt[8], vt[8];
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
-            kt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
-            vt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
+            kt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
+            vt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
         }
         // row statistics of tile p in st, of tile p + 1 fetched during step p
         const float* stat = h ? Dh : Lh;
@@ -322,9 +323,9 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
             const int q0 = q_begin + p * BR;
             fetch2(q0 + BR, nx);
             if (q0 + BR > N)
-                score_step_diag<true>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
+                score_step_diag<E, true>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
             else
-                score_step_diag<false>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
+                score_step_diag<E, false>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
             st[0] = nx[0];
             st[1] = nx[1];
             __builtin_amdgcn_s_waitcnt(kLgkmOnly);
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
                 const int q0 = q_begin + p * BR;
                 fetch2(q0 + BR, nx);
                 if (q0 + BR > N)
-                    score_step<true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
+                    score_step<E, true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
                 else
-                    score_step<false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
+                    score_step<E, false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
                 st[0] = nx[0];
                 st[1] = nx[1];
             }
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
                 cp.copy(j, dOh, qn, N, lq + (OFF_DO - OFF_Q));
             }
         }
-        if (p >= 1) grad_step(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, ob0, ob1, l);
+        if (p >= 1) grad_step<E>(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, ob0, ob1, l);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -378,41 +379,49 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     for (int kg = 0; kg < 4; ++kg) {
         const int kk = k0 + 32 * kg + n;
         if (kk >= N) continue;
-        bf16_t* dKr = dK + hoff + (long long)kk * D;
-        bf16_t* dVr = dV + hoff + (long long)kk * D;
+        e16_t* dKr = dK + hoff + (long long)kk * D;
+        e16_t* dVr = dV + hoff + (long long)kk * D;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
             const int d0 = 32 * r4 + 8 * a4 + 4 * h;
             const int r = 4 * a4;
             uint2 kv, vv;
-            kv.x = pack_bf16x2(accdK[kg][r] * scale, accdK[kg][r + 1] * scale);
-            kv.y = pack_bf16x2(accdK[kg][r + 2] * scale, accdK[kg][r + 3] * scale);
-            vv.x = pack_bf16x2(accdV[kg][r], accdV[kg][r + 1]);
-            vv.y = pack_bf16x2(accdV[kg][r + 2], accdV[kg][r + 3]);
+            kv.x = E::pack2(accdK[kg][r] * scale, accdK[kg][r + 1] * scale);
+            kv.y = E::pack2(accdK[kg][r + 2] * scale, accdK[kg][r + 3] * scale);
+            vv.x = E::pack2(accdV[kg][r], accdV[kg][r + 1]);
+            vv.y = E::pack2(accdV[kg][r + 2], accdV[kg][r + 3]);
             *reinterpret_cast<uint2*>(dKr + d0) = kv;
             *reinterpret_cast<uint2*>(dVr + d0) = vv;
         }
     }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_dkdv_d128(const void* Q, const void* K, const void* V, const void* dO,
-                                const float* L, const float* Dv, void* dK, void* dV, Shape s,
-                                float scale, bool causal, hipStream_t st) {
+template <typename E>
+hipError_t launch_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                       const float* L, const float* Dv, void* dK, void* dV, Shape s, float scale,
+                       bool causal, hipStream_t st) {
     const int nkb = (s.N + BC - 1) / BC;
     const long long nwork = (long long)nkb * s.H * s.B;
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<true>), grid, dim3(NWAVE * 64), 0, st,
-                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO,
-                           L, Dv, (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<E, true>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO,
+                           L, Dv, (e16_t*)dK, (e16_t*)dV, s.N, nkb, scale);
     else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<false>), grid, dim3(NWAVE * 64), 0, st,
-                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO,
-                           L, Dv, (bf16_t*)dK, (bf16_t*)dV, s.N, nkb, scale);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<E, false>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO,
+                           L, Dv, (e16_t*)dK, (e16_t*)dV, s.N, nkb, scale);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dkdv_d128(int dtype, const void* Q, const void* K, const void* V,
+                                const void* dO, const float* L, const float* Dv, void* dK,
+                                void* dV, Shape s, float scale, bool causal, hipStream_t st) {
+    return dtype == DT_F16 ? launch_dkdv<F16E>(Q, K, V, dO, L, Dv, dK, dV, s, scale, causal, st)
+                           : launch_dkdv<Bf16E>(Q, K, V, dO, L, Dv, dK, dV, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -54,7 +54,7 @@ static_assert(LDS_BYTES == 144 * 1024, "LDS plan");
 
 // dS of accumulator elements r, r + 1 as one packed bf16 pair.  MASK applies
 // key > query (causal) and key >= N element by element.
-template <bool MASK, bool CAUSAL>
+template <typename E, bool MASK, bool CAUSAL>
 __device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
                                             float Lq, float Dq, int krow, int q, int N) {
     float d[2];
@@ -68,7 +68,7 @@ __device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& d
         }
         d[u] = __builtin_amdgcn_exp2f(x) * (dP[e] - Dq);
     }
-    return pack_bf16x2(d[0], d[1]);
+    return E::pack2(d[0], d[1]);
 }
 
 // Score role: dS of key block k0 for this wave's 32 queries, stored as slabs
@@ -77,10 +77,10 @@ __device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& d
 // half 1 are interleaved with the dS arithmetic of half 0 (order pinned with
 // sched_barrier).  Masked blocks (at most two per workgroup) keep the plain
 // order, which needs fewer registers.
-template <bool MASK, bool CAUSAL>
+template <typename E, bool MASK, bool CAUSAL>
 __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vbuf, int dbuf,
                                            int k0, int q, int N, float sc, float Lq, float Dq,
-                                           const bf16x8_t (&qt)[8], const bf16x8_t (&gt)[8],
+                                           const v16x8_t (&qt)[8], const v16x8_t (&gt)[8],
                                            const int (&so)[8], int s, int l) {
     const int h = l >> 5, n = l & 31;
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
@@ -100,13 +100,13 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
 #pragma unroll
             for (int dk = 0; dk < 8; ++dk) {
                 const int off = tile_off(row, 32 * dk + 16 * h);
-                S = mfma(lds_b128(sK + off), qt[dk], S);
-                dP = mfma(lds_b128(sV + off), gt[dk], dP);
+                S = E::mma(lds_b128(sK + off), qt[dk], S);
+                dP = E::mma(lds_b128(sV + off), gt[dk], dP);
             }
             uint32_t pk[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                pk[j] = ds_pair<MASK, CAUSAL>(S, dP, 2 * j, sc, Lq, Dq, k0 + 32 * mb + 4 * h, q, N);
+                pk[j] = ds_pair<E, MASK, CAUSAL>(S, dP, 2 * j, sc, Lq, Dq, k0 + 32 * mb + 4 * h, q, N);
             store(mb, pk);
         }
         return;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
     // operand of step i (i = 0..15: key half i / 8, d-chunk i % 8); rows
     // 32 + n share row n's swizzle
     auto opoff = [&](int i) { return so[i & 7] + 32 * ROWB * (i >> 3); };
-    bf16x8_t ak[3], av[3];
+    v16x8_t ak[3], av[3];
     ak[0] = lds_b128(sK + opoff(0));
     av[0] = lds_b128(sV + opoff(0));
     ak[1] = lds_b128(sK + opoff(1));
@@ -124,8 +124,8 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
     for (int i = 0; i < 8; ++i) {
         ak[(i + 2) % 3] = lds_b128(sK + opoff(i + 2));
         av[(i + 2) % 3] = lds_b128(sV + opoff(i + 2));
-        S0 = mfma(ak[i % 3], qt[i], S0);
-        dP0 = mfma(av[i % 3], gt[i], dP0);
+        S0 = E::mma(ak[i % 3], qt[i], S0);
+        dP0 = E::mma(av[i % 3], gt[i], dP0);
         __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk[8];
@@ -135,14 +135,14 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
             ak[(i + 2) % 3] = lds_b128(sK + opoff(i + 2));
             av[(i + 2) % 3] = lds_b128(sV + opoff(i + 2));
         }
-        S1 = mfma(ak[i % 3], qt[i - 8], S1);
-        dP1 = mfma(av[i % 3], gt[i - 8], dP1);
-        pk[i - 8] = ds_pair<false, CAUSAL>(S0, dP0, 2 * (i - 8), sc, Lq, Dq, 0, q, N);
+        S1 = E::mma(ak[i % 3], qt[i - 8], S1);
+        dP1 = E::mma(av[i % 3], gt[i - 8], dP1);
+        pk[i - 8] = ds_pair<E, false, CAUSAL>(S0, dP0, 2 * (i - 8), sc, Lq, Dq, 0, q, N);
         __builtin_amdgcn_sched_barrier(0);
     }
     store(0, pk);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pk[j] = ds_pair<false, CAUSAL>(S1, dP1, 2 * j, sc, Lq, Dq, 0, q, N);
+    for (int j = 0; j < 8; ++j) pk[j] = ds_pair<E, false, CAUSAL>(S1, dP1, 2 * j, sc, Lq, Dq, 0, q, N);
     store(1, pk);
 }
 
@@ -152,7 +152,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
 // and that + 8 (rows 16 t + ... share their swizzle).  stage(t) issues part
 // of a later block's copies after step t's products, so that the copies never
 // pile up in the memory pipeline in front of this wave's work.
-template <typename Stage>
+template <typename E, typename Stage>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, int dbuf,
                                           f32x16_t (&acc)[4], int ob0, int ob1, int l,
                                           Stage&& stage) {
@@ -160,7 +160,7 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
     const unsigned char* k0p = sK + ob0;
     const unsigned char* k1p = sK + ob1;
     const unsigned char* sl = smem + OFF_DS + dbuf * DSB + l * 16;
-    bf16x8_t bK[2], aS[2][4];
+    v16x8_t bK[2], aS[2][4];
     auto fetch = [&](int t, int slot) {
         bK[slot] = tr16_pair(k0p + 16 * ROWB * t, k1p + 16 * ROWB * t);
 #pragma unroll
@@ -171,16 +171,16 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
     for (int t = 0; t < 4; ++t) {
         if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
 #pragma unroll
-        for (int qg = 0; qg < 4; ++qg) acc[qg] = mfma(aS[t & 1][qg], bK[t & 1], acc[qg]);
+        for (int qg = 0; qg < 4; ++qg) acc[qg] = E::mma(aS[t & 1][qg], bK[t & 1], acc[qg]);
         stage(t);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-template <bool CAUSAL>
+template <typename E, bool CAUSAL>
 __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    const bf16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
+    const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
+    const e16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
     float* __restrict__ dqa, int N, int nqb, float scale) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     const int qblk = CAUSAL ? nqb - 1 - work % nqb : work % nqb;  // heaviest first
     const int q0 = qblk * BQ;
     const long long hoff = (long long)head * N * D;
-    const bf16_t* Kh = K + hoff;
-    const bf16_t* Vh = V + hoff;
+    const e16_t* Kh = K + hoff;
+    const e16_t* Vh = V + hoff;
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
     const bool score = wave < 4;
@@ -218,11 +218,11 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     // registers never coexist.
     if (score) {
         const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
-        bf16x8_t qt[8], gt[8];
+        v16x8_t qt[8], gt[8];
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
-            qt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
-            gt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * D + 16 * dk + 8 * h));
+            qt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
+            gt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * D + 16 * dk + 8 * h));
         }
         const float Lq = Lg[(long long)head * N + qc] * kLog2e;
         const float Dq = Dg[(long long)head * N + qc];
@@ -232,10 +232,10 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         for (int p = 0; p <= nblk; ++p) {
             if (p < nblk) {
                 if (p < full)
-                    score_step<false, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
+                    score_step<E, false, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
                                               Dq, qt, gt, so, r4, l);
                 else
-                    score_step<true, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
+                    score_step<E, true, CAUSAL>(smem, p % NKB, p % NVB, p & 1, p * BK, q, N, sc, Lq,
                                              Dq, qt, gt, so, r4, l);
             }
             __builtin_amdgcn_s_waitcnt(0);
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         };
         static_assert(TileCopier<BK, NWAVE / 2>::SLICES == 4, "one slice per 16-key step");
         if (p >= 1) {
-            grad_step(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, l, stage);
+            grad_step<E>(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, l, stage);
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) stage(j);
@@ -291,24 +291,32 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         }
 }
 
-}  // namespace
-
-hipError_t launch_bwd_dq_d128(const void* Q, const void* K, const void* V, const void* dO,
-                              const float* L, const float* Dv, float* dqa, Shape s, float scale,
-                              bool causal, hipStream_t st) {
+template <typename E>
+hipError_t launch_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                     const float* Dv, float* dqa, Shape s, float scale, bool causal,
+                     hipStream_t st) {
     const int nqb = (s.N + BQ - 1) / BQ;
     const long long nwork = (long long)nqb * s.H * s.B;
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<true>), grid, dim3(NWAVE * 64), 0, st, (const bf16_t*)Q,
-                           (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv, dqa, s.N,
-                           nqb, scale);
+        hipLaunchKernelGGL((bwd_dq_kernel<E, true>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO, L,
+                           Dv, dqa, s.N, nqb, scale);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<false>), grid, dim3(NWAVE * 64), 0, st, (const bf16_t*)Q,
-                           (const bf16_t*)K, (const bf16_t*)V, (const bf16_t*)dO, L, Dv, dqa, s.N,
-                           nqb, scale);
+        hipLaunchKernelGGL((bwd_dq_kernel<E, false>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO, L,
+                           Dv, dqa, s.N, nqb, scale);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_d128(int dtype, const void* Q, const void* K, const void* V,
+                              const void* dO, const float* L, const float* Dv, float* dqa,
+                              Shape s, float scale, bool causal, hipStream_t st) {
+    return dtype == DT_F16 ? launch_dq<F16E>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st)
+                           : launch_dq<Bf16E>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
 }
 
 }  // namespace fa

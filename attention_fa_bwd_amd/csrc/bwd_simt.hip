@@ -169,6 +169,8 @@ hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* 
                       Shape s, float scale, bool causal, hipStream_t st) {
     return dtype == DT_BF16
                ? bwd_d<bf16_t>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st)
+           : dtype == DT_F16
+               ? bwd_d<f16_t>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st)
                : bwd_d<float>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st);
 }
 

@@ -116,8 +116,9 @@ static hipError_t fwd_d(const void* Q, const void* K, const void* V, void* O, fl
 
 hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, void* O, float* L,
                       Shape s, float scale, bool causal, hipStream_t st) {
-    return dtype == DT_BF16 ? fwd_d<bf16_t>(Q, K, V, O, L, s, scale, causal, st)
-                            : fwd_d<float>(Q, K, V, O, L, s, scale, causal, st);
+    return dtype == DT_BF16  ? fwd_d<bf16_t>(Q, K, V, O, L, s, scale, causal, st)
+           : dtype == DT_F16 ? fwd_d<f16_t>(Q, K, V, O, L, s, scale, causal, st)
+                             : fwd_d<float>(Q, K, V, O, L, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -46,10 +46,10 @@ static_assert(LDS_BYTES == 112 * 1024, "LDS plan");
 constexpr float kLazy = 8.f;             // rebase threshold, log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <bool CAUSAL>
+template <typename E, bool CAUSAL>
 __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    bf16_t* __restrict__ O, float* __restrict__ Lg, int N, int nqb, float scale) {
+    const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
+    e16_t* __restrict__ O, float* __restrict__ Lg, int N, int nqb, float scale) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
@@ -57,8 +57,8 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     const int qblk = CAUSAL ? nqb - 1 - work % nqb : work % nqb;  // heaviest first
     const int q0 = qblk * BQ;
     const long long hoff = (long long)head * N * D;
-    const bf16_t* Kh = K + hoff;
-    const bf16_t* Vh = V + hoff;
+    const e16_t* Kh = K + hoff;
+    const e16_t* Vh = V + hoff;
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
     const int q = q0 + 32 * wave + n;  // this lane's query
@@ -75,10 +75,10 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         }
     }
     const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
-    bf16x8_t qt[8];
+    v16x8_t qt[8];
 #pragma unroll
     for (int dk = 0; dk < 8; ++dk)
-        qt[dk] = as_bf16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
+        qt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     f32x16_t acc[4];  // O^T of d-block db: lane = query, rows 32 db + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
-    bf16x8_t pb[4];   // P^T of the previous block, 16-key step t = 2 mb + hh
+    v16x8_t pb[4];   // P^T of the previous block, 16-key step t = 2 mb + hh
     float mu = -1e30f, lsum = 0.f;
 
     for (int j = 0; j <= nblk; ++j) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
         // 16 steps: S^T product i (key half i / 8, d-chunk i % 8) and O^T product
         // i (16-key step i / 4, d-block i % 4); operands two / one steps ahead
-        bf16x8_t ak[3], av[2];
+        v16x8_t ak[3], av[2];
         auto kop = [&](int i) { return lds_b128(sK + so[i & 7] + 32 * ROWB * (i >> 3)); };
         auto vop = [&](int i) {
             const int t = i >> 2, db = i & 3;
@@ -140,13 +140,13 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
             if (mf) {
                 if (i + 2 < 16) ak[(i + 2) % 3] = kop(i + 2);
                 if (i < 8)
-                    S0 = mfma(ak[i % 3], qt[i], S0);
+                    S0 = E::mma(ak[i % 3], qt[i], S0);
                 else
-                    S1 = mfma(ak[i % 3], qt[i - 8], S1);
+                    S1 = E::mma(ak[i % 3], qt[i - 8], S1);
             }
             if (pv) {
                 if (i + 1 < 16) av[(i + 1) & 1] = vop(i + 1);
-                acc[i & 3] = mfma(av[i & 1], pb[i >> 2], acc[i & 3]);
+                acc[i & 3] = E::mma(av[i & 1], pb[i >> 2], acc[i & 3]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -187,10 +187,10 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
             }
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                pb[t] = as_bf16x8(make_uint4(pack_bf16x2(p[8 * t], p[8 * t + 1]),
-                                             pack_bf16x2(p[8 * t + 2], p[8 * t + 3]),
-                                             pack_bf16x2(p[8 * t + 4], p[8 * t + 5]),
-                                             pack_bf16x2(p[8 * t + 6], p[8 * t + 7])));
+                pb[t] = as_v16x8(make_uint4(E::pack2(p[8 * t], p[8 * t + 1]),
+                                             E::pack2(p[8 * t + 2], p[8 * t + 3]),
+                                             E::pack2(p[8 * t + 4], p[8 * t + 5]),
+                                             E::pack2(p[8 * t + 6], p[8 * t + 7])));
         }
         // block j + 1's copies (issued one phase ago) must have landed; this
         // phase's may stay in flight
@@ -204,38 +204,45 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
     if (q < N) {
         const float inv = 1.f / ltot;
-        bf16_t* orow = O + hoff + (long long)q * D;
+        e16_t* orow = O + hoff + (long long)q * D;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int r = 4 * a4;
                 uint2 v;
-                v.x = pack_bf16x2(acc[db][r] * inv, acc[db][r + 1] * inv);
-                v.y = pack_bf16x2(acc[db][r + 2] * inv, acc[db][r + 3] * inv);
+                v.x = E::pack2(acc[db][r] * inv, acc[db][r + 1] * inv);
+                v.y = E::pack2(acc[db][r + 2] * inv, acc[db][r + 3] * inv);
                 *reinterpret_cast<uint2*>(orow + 32 * db + 8 * a4 + 4 * h) = v;
             }
         if (h == 0) Lg[(long long)head * N + q] = (mu + __builtin_log2f(ltot)) * kLn2;
     }
 }
 
-}  // namespace
-
-hipError_t launch_fwd_d128(const void* Q, const void* K, const void* V, void* O, float* L,
+template <typename E>
+hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O, float* L,
                            Shape s, float scale, bool causal, hipStream_t st) {
     const int nqb = (s.N + BQ - 1) / BQ;
     const long long nwork = (long long)nqb * s.H * s.B;
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((fwd_mfma_kernel<true>), grid, dim3(NWAVE * 64), 0, st,
-                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, L,
-                           s.N, nqb, scale);
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, true>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
+                           nqb, scale);
     else
-        hipLaunchKernelGGL((fwd_mfma_kernel<false>), grid, dim3(NWAVE * 64), 0, st,
-                           (const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, (bf16_t*)O, L,
-                           s.N, nqb, scale);
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, false>), grid, dim3(NWAVE * 64), 0, st,
+                           (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
+                           nqb, scale);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_d128(int dtype, const void* Q, const void* K, const void* V, void* O,
+                           float* L, Shape s, float scale, bool causal, hipStream_t st) {
+    return dtype == DT_F16 ? launch_fwd_mfma<F16E>(Q, K, V, O, L, s, scale, causal, st)
+                           : launch_fwd_mfma<Bf16E>(Q, K, V, O, L, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -23,7 +23,11 @@
 namespace fa {
 namespace mf {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+// Eight 16-bit elements: one matrix-core operand per lane.  The vector is
+// declared with bf16 elements; fp16 operands are carried in it as bit patterns
+// and reinterpreted at the fp16 product.
+typedef __bf16 v16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -40,23 +44,43 @@ constexpr int kLgkmOnly = 0xC07F;
 constexpr int kVmcnt8Lgkm0 = 0x0078;
 constexpr int kVmcnt4Lgkm0 = 0x0074;
 constexpr int D = 128;       // head dim of the matrix-core kernels
-constexpr int ROWB = D * 2;  // bytes per bf16 row of Q, K, V, dO
+constexpr int ROWB = D * 2;  // bytes per 16-bit row of Q, K, V, dO
 
-__device__ __forceinline__ f32x16_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+__device__ __forceinline__ f32x16_t mfma(const v16x8_t& a, const v16x8_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+// Element types of the matrix-core kernels: the product instruction and the
+// fp32 -> element packing (round to nearest even).
+struct Bf16E {
+    static constexpr int dtype = DT_BF16;
+    static __device__ __forceinline__ f32x16_t mma(const v16x8_t& a, const v16x8_t& b,
+                                                   const f32x16_t& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_bf16x2(a, b); }
+};
+struct F16E {
+    static constexpr int dtype = DT_F16;
+    static __device__ __forceinline__ f32x16_t mma(const v16x8_t& a, const v16x8_t& b,
+                                                   const f32x16_t& c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float a, float b) { return pack_f16x2(a, b); }
+};
 
-__device__ __forceinline__ bf16x8_t lds_b128(const unsigned char* p) {
-    return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+__device__ __forceinline__ v16x8_t as_v16x8(const uint4& u) { return __builtin_bit_cast(v16x8_t, u); }
+
+__device__ __forceinline__ v16x8_t lds_b128(const unsigned char* p) {
+    return as_v16x8(*reinterpret_cast<const uint4*>(p));
 }
 
 // Two transposing 8-byte LDS reads combined into one 8-element operand.
-__device__ __forceinline__ bf16x8_t tr16_pair(const unsigned char* p0, const unsigned char* p1) {
+__device__ __forceinline__ v16x8_t tr16_pair(const unsigned char* p0, const unsigned char* p1) {
     i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4_t, p0));
     i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(FA_LDS(i16x4_t, p1));
-    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(v16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // 16-byte chunk swizzle of a 256-byte row (16 chunks), XORed into the chunk
@@ -93,14 +117,14 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// Copy rows [r0, r0 + nrows) of a [N, 128] bf16 matrix into a swizzled LDS
+// Copy rows [r0, r0 + nrows) of a [N, 128] 16-bit matrix into a swizzled LDS
 // tile with direct-to-LDS loads: each wave moves 1 KiB (64 lanes x 16 bytes)
 // per instruction, lane i landing at byte 16 i of the wave's slice, so lane i
 // fetches the logical chunk that the swizzle places there.  Rows at or beyond
 // N are clamped to row N - 1 (finite data; callers make them contribute 0).
 // UNTRACKED: issue through lds_copy16 (the caller waits before use).
 template <int NROWS, int NWAVES, bool UNTRACKED = false>
-__device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t* src, int r0,
+__device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const e16_t* src, int r0,
                                            int N, int wave, int lane) {
     constexpr int BYTES = NROWS * ROWB;
     constexpr int PER_WAVE = BYTES / NWAVES;
@@ -112,7 +136,7 @@ __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const bf16_t
         const int chunk = ((p % ROWB) >> 4) ^ swz(row);
         int g = r0 + row;
         g = g < N ? g : N - 1;
-        const bf16_t* gp = src + (long long)g * D + chunk * 8;
+        const e16_t* gp = src + (long long)g * D + chunk * 8;
         unsigned char* lp = lds_tile + wave * PER_WAVE + j * 1024;
         if (UNTRACKED)
             lds_copy16(gp, __builtin_amdgcn_readfirstlane(
@@ -133,7 +157,7 @@ __device__ __forceinline__ void lds_copy16_sbase(const void* base, uint32_t voff
 }
 #pragma clang diagnostic pop
 
-// Copies NROWS-row tiles of [N, 128] bf16 matrices into swizzled LDS tiles
+// Copies NROWS-row tiles of [N, 128] 16-bit matrices into swizzled LDS tiles
 // with NWAVES waves, one 1 KiB slice (one direct-to-LDS copy) at a time, so
 // that the copies of a tile can be spread over the work of a loop iteration.
 // The per-lane byte offsets of the slices are computed once; a full tile then
@@ -161,7 +185,7 @@ struct TileCopier {
         }
     }
     // slice j of rows [r0, r0 + NROWS) of src into the LDS tile at byte lds_tile
-    __device__ __forceinline__ void copy(int j, const bf16_t* src, int r0, int N,
+    __device__ __forceinline__ void copy(int j, const e16_t* src, int r0, int N,
                                          uint32_t lds_tile) const {
         const uint32_t lds = lds_tile + lds_wave + j * 1024;
         if (r0 + NROWS <= N) {

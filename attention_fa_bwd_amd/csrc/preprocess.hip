@@ -56,8 +56,13 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
                 make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
         } else {
             uint2 p;
-            p.x = pack_bf16x2(v.x * scale, v.y * scale);
-            p.y = pack_bf16x2(v.z * scale, v.w * scale);
+            if constexpr (__is_same(T, f16_t)) {
+                p.x = pack_f16x2(v.x * scale, v.y * scale);
+                p.y = pack_f16x2(v.z * scale, v.w * scale);
+            } else {
+                p.x = pack_bf16x2(v.x * scale, v.y * scale);
+                p.y = pack_bf16x2(v.z * scale, v.w * scale);
+            }
             reinterpret_cast<uint2*>(dst)[i] = p;
         }
     }
@@ -94,8 +99,9 @@ static hipError_t pre_d(const void* O, const void* dO, float* Dv, float* dqa, Sh
 
 hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D,
                              float* dq_accum, Shape s, hipStream_t st) {
-    return dtype == DT_BF16 ? pre_d<bf16_t>(O, dO, D, dq_accum, s, st)
-                            : pre_d<float>(O, dO, D, dq_accum, s, st);
+    return dtype == DT_BF16  ? pre_d<bf16_t>(O, dO, D, dq_accum, s, st)
+           : dtype == DT_F16 ? pre_d<f16_t>(O, dO, D, dq_accum, s, st)
+                             : pre_d<float>(O, dO, D, dq_accum, s, st);
 }
 
 hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s, float scale,
@@ -105,6 +111,9 @@ hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s
     if (dtype == DT_BF16)
         hipLaunchKernelGGL((convert_kernel<bf16_t>), dim3(g), dim3(256), 0, st, dq_accum,
                            (bf16_t*)dQ, n4, scale);
+    else if (dtype == DT_F16)
+        hipLaunchKernelGGL((convert_kernel<f16_t>), dim3(g), dim3(256), 0, st, dq_accum,
+                           (f16_t*)dQ, n4, scale);
     else
         hipLaunchKernelGGL((convert_kernel<float>), dim3(g), dim3(256), 0, st, dq_accum,
                            (float*)dQ, n4, scale);

@@ -17,8 +17,11 @@
  *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d] row-major
  *              (d fastest) in the element type `dtype`.  L, D: contiguous
  *              [B, H, N] fp32.  dq_accum: contiguous [B, H, N, d] fp32.
- *   dtype      FA_DTYPE_F32 (IEEE float) or FA_DTYPE_BF16 (bfloat16 bits).
- *              L, D and dq_accum are always fp32.
+ *   dtype      FA_DTYPE_F32 (IEEE float), FA_DTYPE_BF16 (bfloat16 bits) or
+ *              FA_DTYPE_F16 (IEEE half bits).  L, D and dq_accum are always
+ *              fp32.  16-bit outputs are rounded to nearest even.  In fp16 the
+ *              kernels hold P and dS as fp16 operands: inputs whose dS would
+ *              exceed the half range (|dS| > 65504) are outside the contract.
  *   Scores     S_ij = scale * Q_i . K_j; L_i = log sum_j exp(S_ij) over the
  *              visible keys (natural log).  causal != 0 hides key j from
  *              query i when j > i (0-based, diagonal kept).
@@ -47,7 +50,7 @@
 extern "C" {
 #endif
 
-typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+typedef enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_F16 = 2 } fa_dtype_t;
 
 typedef enum {
     FA_OK = 0,
@@ -63,8 +66,8 @@ typedef enum {
  * alpha = exp(m - m') at each key block), O = a / l and L = m + log l
  * (1point3acres post "手扒了FlashAttention", the online-softmax recurrence and
  * the logsumexp; FA2 chapter 16 sec 16.4).  Supporting step of the backward:
- * it provides O and L for benchmarking and end-to-end checks.  bf16 with
- * d = 128 runs on the matrix cores and rebases lazily (only when a block's
+ * it provides O and L for benchmarking and end-to-end checks.  bf16 and fp16
+ * with d = 128 run on the matrix cores and rebase lazily (only when a block's
  * maximum exceeds the running one by more than a factor 2^8, which leaves
  * O and L unchanged in exact arithmetic); other cases run a vector-ALU kernel.
  *   in : Q, K, V [B,H,N,d] dtype
@@ -95,7 +98,7 @@ int fa_bwd_preprocess(int dtype, const void* O, const void* dO,
  * 16.6); under the causal mask, tiles wholly above the diagonal are skipped
  * (sec 16.8 item 2).  dQ = dS K, unscaled, ends up in the fp32 dq_accum buffer
  * (sec 16.3).
- *   bf16, d = 128: two matrix-core passes, fa_bwd_dq then fa_bwd_dkdv (below);
+ *   bf16 / fp16, d = 128: two matrix-core passes, fa_bwd_dq then fa_bwd_dkdv;
  *                  dq_accum is overwritten, every output is bitwise
  *                  reproducible.
  *   other pairs:   one vector-ALU kernel that adds dQ partials into dq_accum
@@ -112,7 +115,8 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V,
            void* stream);
 
 /*
- * fa_bwd_dkdv / fa_bwd_dq -- the two passes fa_bwd runs for bf16 with d = 128,
+ * fa_bwd_dkdv / fa_bwd_dq -- the two passes fa_bwd runs for bf16 and fp16 with
+ * d = 128,
  * callable on their own (same arguments and layouts as fa_bwd).  FA2 chapter
  * 16 sec 16.3 weighs fp32 global atomics for dQ against a second kernel; on
  * MI355X the atomics measured too slow (about 340 G fp32 atomics/s), so dQ has
@@ -136,7 +140,7 @@ int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V,
 
 /*
  * fa_bwd_convert_dq -- dQ = scale * dq_accum cast to dtype (round to nearest
- * even for bf16) (FA2 chapter 16 sec 16.3: the separate kernel that applies
+ * even for bf16 and fp16) (FA2 chapter 16 sec 16.3: the separate kernel that applies
  * the softmax scale and converts the fp32 accumulation buffer).
  *   in : dq_accum [B,H,N,d] fp32
  *   out: dQ [B,H,N,d] dtype

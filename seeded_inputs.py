@@ -29,7 +29,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str            # "fp32" or "bf16"
+    dtype: str            # "fp32", "bf16" or "fp16"
     causal: tuple         # causal modes this workload is run in
     seed: int
     q_mult: float = 1.0   # applied to Q after drawing (exact in bf16 for powers of two)
@@ -71,12 +71,24 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE half (round-to-nearest-even; beyond the largest
+    half, infinity), returned as uint16 bits."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of IEEE half bit patterns to float32."""
+    return np.ascontiguousarray(b, dtype=np.uint16).view(np.float16).astype(np.float32)
+
+
 @dataclass
 class Inputs:
     """Q, K, V, dO as float32 arrays holding exactly representable values.
 
-    For bf16 workloads ``bits`` holds the uint16 patterns that go to the GPU and
-    the float32 arrays are their exact widening.
+    For bf16 and fp16 workloads ``bits`` holds the uint16 patterns that go to
+    the GPU and the float32 arrays are their exact widening.
     """
     wl: Workload
     Q: np.ndarray
@@ -106,6 +118,10 @@ def draw(wl: Workload, *, B=None, H=None, N=None, d=None, seed=None, q_mult=None
     if dtype == "bf16":
         bits = {n: f32_to_bf16_bits(a) for n, a in zip(names, arrs)}
         vals = [bf16_bits_to_f32(bits[n]) for n in names]
+        return Inputs(wl2, *vals, bits=bits)
+    if dtype == "fp16":
+        bits = {n: f32_to_f16_bits(a) for n, a in zip(names, arrs)}
+        vals = [f16_bits_to_f32(bits[n]) for n in names]
         return Inputs(wl2, *vals, bits=bits)
     if dtype == "fp32":
         return Inputs(wl2, *arrs)

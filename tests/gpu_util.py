@@ -17,8 +17,8 @@ import attention_fa_bwd_amd as fa
 import oracle
 import seeded_inputs as si
 
-TOL = {"fp32": 1e-5, "bf16": 2e-2}
-TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16}
+TOL = {"fp32": 1e-5, "bf16": 2e-2, "fp16": 1e-2}
+TORCH_DT = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}
 
 
 def note(msg: str) -> None:
@@ -28,9 +28,9 @@ def note(msg: str) -> None:
 
 
 def upload(inp: si.Inputs, name: str) -> torch.Tensor:
-    if inp.wl.dtype == "bf16":
+    if inp.wl.dtype in ("bf16", "fp16"):
         b = np.ascontiguousarray(inp.bits[name]).view(np.int16)
-        return torch.from_numpy(b).view(torch.bfloat16).cuda()
+        return torch.from_numpy(b).view(TORCH_DT[inp.wl.dtype]).cuda()
     return torch.from_numpy(np.ascontiguousarray(getattr(inp, name))).cuda()
 
 

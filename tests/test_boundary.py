@@ -75,14 +75,16 @@ def test_unsupported_head_dim(d):
     assert lib.fa_bwd_convert_dq(1, p, p, 1, 1, 8, d, 0.1, None) == fa.FA_EUNSUPPORTED
 
 
-def test_split_passes_only_for_bf16_d128():
+def test_split_passes_only_for_16bit_d128():
     lib = fa.load()
     p = ALIGNED
-    for dtype, d in ((0, 128), (1, 64), (0, 16)):
+    assert _bwd(lib, dtype=3) == fa.FA_EINVAL
+    for dtype, d in ((0, 128), (1, 64), (0, 16), (2, 64), (2, 32)):
         assert lib.fa_bwd_dkdv(dtype, p, p, p, p, p, p, p, p, 1, 1, 8, d, 0.1, 0, None) == fa.FA_EUNSUPPORTED
         assert lib.fa_bwd_dq(dtype, p, p, p, p, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_bwd_dkdv(1, p, None, p, p, p, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
     assert lib.fa_bwd_dq(1, p, p, p, p, p, p, None, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_dkdv(2, p, None, p, p, p, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
 
 
 def test_binding_rejects_cpu_tensors():

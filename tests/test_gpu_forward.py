@@ -1,10 +1,10 @@
 """GPU parity of the forward (fa_fwd_lse): O and L against the oracle's plain
 definition, element by element.
 
-bf16 with d = 128 runs the matrix-core kernel (lazy rebase of the running
+bf16 and fp16 with d = 128 run the matrix-core kernel (lazy rebase of the running
 maximum); the other cases run the vector-ALU kernel.  Tolerances: O within the
-bf16 / fp32 bar (max |err| / max |ref|), L (natural log, fp32) within 1e-4
-absolute -- S comes from exact bf16 products accumulated in fp32, so L is
+element type's bar (max |err| / max |ref|), L (natural log, fp32) within 1e-4
+absolute -- S comes from exact 16-bit products accumulated in fp32, so L is
 accurate to a few fp32 ulps of the scores."""
 import numpy as np
 import pytest
@@ -34,22 +34,23 @@ def _check(inp, causal, what, l_tol=1e-4):
     assert el <= l_tol, f"{what}: L abs err {el:.3e}"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 200, 255, 256, 257, 600])
-def test_bf16_d128_shapes(N, causal):
+def test_d128_shapes(N, causal, dtype):
     """Matrix-core forward: tiny, ragged and multi-block N (the workgroup holds
     256 queries, key blocks are 64 rows)."""
-    gu.note(f"case fwd bf16 d=128 N={N} causal={causal}")
-    inp = si.draw_custom(2, 2, N, 128, "bf16", seed=300 + N)
+    gu.note(f"case fwd {dtype} d=128 N={N} causal={causal}")
+    inp = si.draw_custom(2, 2, N, 128, dtype, seed=300 + N)
     _check(inp, causal, f"N={N}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d,dtype", [(16, "fp32"), (64, "bf16"), (128, "fp32")])
+@pytest.mark.parametrize("d,dtype", [(16, "fp32"), (64, "bf16"), (64, "fp16"), (128, "fp32")])
 def test_vector_alu_forward(d, dtype, causal):
     gu.note(f"case fwd {dtype} d={d} causal={causal}")
     inp = si.draw_custom(1, 2, 133, d, dtype, seed=400 + d)
-    _check(inp, causal, f"{dtype} d={d}", l_tol=1e-4 if dtype == "bf16" else 1e-6)
+    _check(inp, causal, f"{dtype} d={d}", l_tol=1e-6 if dtype == "fp32" else 1e-4)
 
 
 @pytest.mark.parametrize("q_mult", [4.0, 8.0])
