@@ -1,7 +1,8 @@
 // mfma_common.hpp -- CDNA4 (gfx950) matrix-core helpers shared by the two
 // backward kernels (key-outer dK/dV, query-outer dQ).
 //
-// Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the hardware):
+// Operand layouts of v_mfma_f32_32x32x16_bf16 and _f16 (the same; checked on
+// the hardware):
 //   A (32 x 16, M x K): lane l holds row l % 32, k = 8 (l / 32) + 0..7
 //   B (16 x 32, K x N): lane l holds column l % 32, k = 8 (l / 32) + 0..7
 //   C (32 x 32):        lane l holds column l % 32, row 8 (r / 4) + 4 (l / 32) + r % 4

@@ -153,6 +153,27 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     }
 
 
+def forward_time(wl, causal: bool, inputs, reps: int = 5):
+    """Time of the forward alone (not part of a step): HIP events around
+    `reps` calls on the launch stream after one warm-up call."""
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    q, k, v = inputs
+    o = torch.empty_like(q)
+    L = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fa.fa_fwd_lse(q, k, v, o, L, wl.scale, causal, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fa.fa_fwd_lse(q, k, v, o, L, wl.scale, causal, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(wl, causal: bool, budget_s: float):
     """The oracle's full backward (by definition) on a bounded sample of heads."""
     import numpy as np
@@ -210,6 +231,10 @@ def main():
             r["kernels"][name] = {"avg_launch_ms": round(ms, 4), "flop_per_launch": kflop,
                                   "achieved": round(kflop / (ms * 1e-3) / 1e12, 3),
                                   "frac": round(kflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        fms = forward_time(wl, causal, (up["Q"], up["K"], up["V"]))
+        ffl = 0.4 * flops  # 4·B·H·N²·d (×½ causal)
+        r["forward"] = {"ms": round(fms, 4), "tflops": round(ffl / (fms * 1e-3) / 1e12, 3),
+                        "bwd_over_fwd_time": round(r["ms_per_step"] / fms, 3)}
         results[causal] = r
         del o, L
     prim = results[args.causal]
@@ -240,6 +265,7 @@ def main():
                      "flop_per_launch": kd["flop_per_launch"],
                      "avg_launch_ms": kd["avg_launch_ms"]},
         "kernels": prim["kernels"],
+        "forward": prim["forward"],
     }
     if len(results) > 1:
         other = results[not args.causal]
@@ -247,7 +273,7 @@ def main():
             "value": round(other["tflops"], 3), "ms_per_step": round(other["ms_per_step"], 4),
             "pct_bf16_peak": round(other["pct_peak"], 2),
             "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
-            "kernels": other["kernels"]}
+            "kernels": other["kernels"], "forward": other["forward"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
     else:
