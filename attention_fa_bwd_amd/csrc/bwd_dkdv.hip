@@ -19,11 +19,12 @@
 //     dP = dO V^T (query on rows, key on lanes), P = exp2(S scale log2(e) -
 //     L log2(e)) and dS = P (dP - D), and store P and dS (bf16) to LDS in
 //     their own register order, one 1 KiB slab per (16-query step, key group);
-//   * gradient waves 4..7 own rows [32 g, 32 g + 32) of d of dV^T and dK^T for
-//     all 128 keys (accumulators in registers).  One tile behind the score
-//     waves, they read dO^T and Q^T fragments of that tile with
-//     ds_read_b64_tr_b16 -- each fragment feeds four products, one per key
-//     group -- and P and dS straight from the slabs;
+//   * gradient waves 4..7 own one output each, dV^T (waves 4, 5) or dK^T
+//     (waves 6, 7), for rows [64 (g % 2), +64) of d and all 128 keys
+//     (accumulators in registers).  One tile behind the score waves, they
+//     read dO^T or Q^T fragments of that tile with ds_read_b64_tr_b16 -- each
+//     fragment feeds four products, one per key group -- and P or dS straight
+//     from the slabs, each slab feeding two products;
 //   * Q and dO tiles (64 rows, swizzled 256-byte rows) rotate through three
 //     LDS buffers (score waves read tile p, gradient waves tile p - 1, loads
 //     fill tile p + 1 with direct-to-LDS copies); P and dS through two.  One
@@ -216,38 +217,38 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
     }
 }
 
-// Gradient role: dV^T += dO^T P and dK^T += Q^T dS for this wave's 32 rows of
-// d; the next 16-query step's operands are read while the current step's
-// products issue.  ob0 / ob1: the lane's transposing-read offsets for rows
-// 4 h + (l % 16) / 4 and that + 8 (rows 16 t + ... share their swizzle).
+// Gradient role: one output per wave -- dV^T += dO^T P (DK = false) or
+// dK^T += Q^T dS (DK = true) -- for 64 rows of d (two 32-row blocks) and all
+// 128 keys, so each P or dS slab is read by two waves.  Operands of a
+// 16-query step: two transposing-read pairs (one per d block, each feeding
+// four products) and four slabs (one per key group, each feeding two), read
+// two steps ahead.  ob0 / ob1: the lane's transposing-read offsets of rows
+// 4 h + (l % 16) / 4 and that + 8 in each d block (rows 16 t + ... share
+// their swizzle).
 template <typename E>
-__device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf,
-                                          f32x16_t (&accdV)[4], f32x16_t (&accdK)[4], int ob0,
-                                          int ob1, int l) {
-    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
-    const unsigned char* q0p = sQ + ob0;
-    const unsigned char* q1p = sQ + ob1;
-    const unsigned char* sl = smem + OFF_P + pbuf * PDS + l * 16;
-    constexpr int DOQ = OFF_DO - OFF_Q, DSP = OFF_DS - OFF_P;
-    v16x8_t aO[2], aQ[2], bP[2][4], bS[2][4];
+__device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf, bool dk,
+                                          f32x16_t (&acc)[2][4], const int (&ob0)[2],
+                                          const int (&ob1)[2], int l) {
+    const unsigned char* sA = smem + (dk ? OFF_Q : OFF_DO) + qbuf * TILE;
+    const unsigned char* sl = smem + (dk ? OFF_DS : OFF_P) + pbuf * PDS + l * 16;
+    v16x8_t a[3][2], b[3][4];
     auto fetch = [&](int t, int slot) {
-        aO[slot] = tr16_pair(q0p + DOQ + 16 * ROWB * t, q1p + DOQ + 16 * ROWB * t);
-        aQ[slot] = tr16_pair(q0p + 16 * ROWB * t, q1p + 16 * ROWB * t);
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-            bP[slot][kg] = lds_b128(sl + (t * 4 + kg) * SLAB);
-            bS[slot][kg] = lds_b128(sl + DSP + (t * 4 + kg) * SLAB);
-        }
+        for (int db = 0; db < 2; ++db)
+            a[slot][db] = tr16_pair(sA + ob0[db] + 16 * ROWB * t, sA + ob1[db] + 16 * ROWB * t);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) b[slot][kg] = lds_b128(sl + (t * 4 + kg) * SLAB);
     };
     fetch(0, 0);
+    fetch(1, 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-        if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
+        if (t + 2 < 4) fetch(t + 2, (t + 2) % 3);
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-            accdV[kg] = E::mma(aO[t & 1], bP[t & 1][kg], accdV[kg]);
-            accdK[kg] = E::mma(aQ[t & 1], bS[t & 1][kg], accdK[kg]);
-        }
+        for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+                acc[db][kg] = E::mma(a[t % 3][db], b[t % 3][kg], acc[db][kg]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -349,14 +350,26 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
         return;
     }
 
-    f32x16_t accdV[4], accdK[4];
+    // gradient wave r4: dV (r4 < 2) or dK (r4 >= 2) for rows [64 (r4 & 1), +64) of d
+    const bool is_dk = r4 >= 2;
+    const int dh = r4 & 1;
+    f32x16_t acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) accdV[i] = accdK[i] = f32x16_t{};
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
     const TileCopier<BR, NWAVE / 2> cp(r4, l);
     const uint32_t lds0 = lds_addr(smem);
-    const int g2 = (l >> 4) & 1, colb = 64 * r4 + 32 * g2 + 8 * (l & 3);
-    const int x = 4 * h + ((l & 15) >> 2);
-    const int ob0 = tile_off(x, colb), ob1 = tile_off(x + 8, colb);
+    int ob0[2], ob1[2];
+    {
+        const int g2 = (l >> 4) & 1, x = 4 * h + ((l & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int colb = 64 * (2 * dh + db) + 32 * g2 + 8 * (l & 3);
+            ob0[db] = tile_off(x, colb);
+            ob1[db] = tile_off(x + 8, colb);
+        }
+    }
     for (int p = 0; p <= ntiles; ++p) {
         // copies of tile p + 1 first: they need the whole phase to land
         if (p + 1 < ntiles) {
@@ -368,31 +381,31 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
                 cp.copy(j, dOh, qn, N, lq + (OFF_DO - OFF_Q));
             }
         }
-        if (p >= 1) grad_step<E>(smem, (p - 1) % 3, (p - 1) & 1, accdV, accdK, ob0, ob1, l);
+        if (p >= 1) grad_step<E>(smem, (p - 1) % 3, (p - 1) & 1, is_dk, acc, ob0, ob1, l);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
-    // epilogue: accumulator kg holds dV^T / dK^T for keys k0 + 32 kg + n,
-    // rows of d 32 g + 8 (r / 4) + 4 h + r % 4
+    // epilogue: acc[db][kg] holds dV^T or dK^T for keys k0 + 32 kg + n, rows
+    // of d 32 (2 dh + db) + 8 (r / 4) + 4 h + r % 4
+    e16_t* out = is_dk ? dK : dV;
+    const float osc = is_dk ? scale : 1.f;
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
         const int kk = k0 + 32 * kg + n;
         if (kk >= N) continue;
-        e16_t* dKr = dK + hoff + (long long)kk * D;
-        e16_t* dVr = dV + hoff + (long long)kk * D;
+        e16_t* row = out + hoff + (long long)kk * D;
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-            const int d0 = 32 * r4 + 8 * a4 + 4 * h;
-            const int r = 4 * a4;
-            uint2 kv, vv;
-            kv.x = E::pack2(accdK[kg][r] * scale, accdK[kg][r + 1] * scale);
-            kv.y = E::pack2(accdK[kg][r + 2] * scale, accdK[kg][r + 3] * scale);
-            vv.x = E::pack2(accdV[kg][r], accdV[kg][r + 1]);
-            vv.y = E::pack2(accdV[kg][r + 2], accdV[kg][r + 3]);
-            *reinterpret_cast<uint2*>(dKr + d0) = kv;
-            *reinterpret_cast<uint2*>(dVr + d0) = vv;
-        }
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int d0 = 32 * (2 * dh + db) + 8 * a4 + 4 * h;
+                const int r = 4 * a4;
+                uint2 v;
+                v.x = E::pack2(acc[db][kg][r] * osc, acc[db][kg][r + 1] * osc);
+                v.y = E::pack2(acc[db][kg][r + 2] * osc, acc[db][kg][r + 3] * osc);
+                *reinterpret_cast<uint2*>(row + d0) = v;
+            }
     }
 }
 
