@@ -244,6 +244,10 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         if (t + 2 < 4) fetch(t + 2, (t + 2) % 3);
+        // the reads ahead go out before this step's products, which then run
+        // back to back (left to itself the compiler threads the reads through
+        // the products with a wait before nearly every one)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg)
 #pragma unroll
@@ -371,15 +375,16 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
         }
     }
     for (int p = 0; p <= ntiles; ++p) {
-        // copies of tile p + 1 first: they need the whole phase to land
-        if (p + 1 < ntiles) {
-            const int qn = q_begin + (p + 1) * BR;
-            const uint32_t lq = lds0 + OFF_Q + ((p + 1) % 3) * TILE;
+        // copies of tile p + 1 first: they need the whole phase to land.  In
+        // the last two phases the buffer they fill is read by no one; they
+        // are issued all the same (rows clamped into range), which keeps the
+        // loop free of branches around them -- measurably faster.
+        const int qn = q_begin + (p + 1) * BR;
+        const uint32_t lq = lds0 + OFF_Q + ((p + 1) % 3) * TILE;
 #pragma unroll
-            for (int j = 0; j < cp.SLICES; ++j) {
-                cp.copy(j, Qh, qn, N, lq);
-                cp.copy(j, dOh, qn, N, lq + (OFF_DO - OFF_Q));
-            }
+        for (int j = 0; j < cp.SLICES; ++j) {
+            cp.copy(j, Qh, qn, N, lq);
+            cp.copy(j, dOh, qn, N, lq + (OFF_DO - OFF_Q));
         }
         if (p >= 1) grad_step<E>(smem, (p - 1) % 3, (p - 1) & 1, is_dk, acc, ob0, ob1, l);
         __builtin_amdgcn_s_waitcnt(0);

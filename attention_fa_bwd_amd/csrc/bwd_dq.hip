@@ -170,6 +170,9 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         if (t + 1 < 4) fetch(t + 1, (t + 1) & 1);
+        // the next step's reads go out before this step's products, which
+        // then run back to back
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qg = 0; qg < 4; ++qg) acc[qg] = E::mma(aS[t & 1][qg], bK[t & 1], acc[qg]);
         stage(t);
@@ -254,16 +257,16 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     const int ob0 = tile_off(x, colb), ob1 = tile_off(x + 8, colb);
     for (int p = 0; p <= nblk; ++p) {
         // copies of block p + 2 first; block p + 1's (issued one phase ago)
-        // must have landed by the barrier, these may stay in flight
-        const bool more = p + 2 < nblk;
+        // must have landed by the barrier, these may stay in flight.  Past
+        // the last block the buffers they fill are read by no one; they are
+        // issued all the same (rows clamped into range), which keeps the
+        // products free of branches around them.
         const int kn = (p + 2) * BK;
         const uint32_t lk = lds0 + OFF_K + ((p + 2) % NKB) * TILE;
         const uint32_t lv = lds0 + OFF_V + ((p + 2) % NVB) * TILE;
         auto stage = [&](int j) {
-            if (more) {
-                cp.copy(j, Kh, kn, N, lk);
-                cp.copy(j, Vh, kn, N, lv);
-            }
+            cp.copy(j, Kh, kn, N, lk);
+            cp.copy(j, Vh, kn, N, lv);
         };
         static_assert(TileCopier<BK, NWAVE / 2>::SLICES == 4, "one slice per 16-key step");
         if (p >= 1) {
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) stage(j);
         }
-        if (more)
+        if (p < nblk)
             __builtin_amdgcn_s_waitcnt(kVmcnt8Lgkm0);
         else
             __builtin_amdgcn_s_waitcnt(0);

@@ -107,8 +107,10 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     float mu = -1e30f, lsum = 0.f;
 
     for (int j = 0; j <= nblk; ++j) {
-        const bool more = j + SD < nblk;
-        if (more) {
+        // copies of block j + SD; past the last block the buffers they fill
+        // are read by no one, and they are issued all the same (rows clamped
+        // into range) to keep the loop free of branches around them
+        {
             const int kn = (j + SD) * BK;
             const uint32_t lk = lds0 + OFF_K + ((j + SD) % NKB) * TILE;
             const uint32_t lv = lds0 + OFF_V + ((j + SD) % NVB) * TILE;
@@ -194,7 +196,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         }
         // block j + 1's copies (issued one phase ago) must have landed; this
         // phase's may stay in flight
-        if (more)
+        if (j < nblk)
             __builtin_amdgcn_s_waitcnt(kVmcnt4Lgkm0);
         else
             __builtin_amdgcn_s_waitcnt(0);

@@ -162,9 +162,9 @@ __device__ __forceinline__ void lds_copy16_sbase(const void* base, uint32_t voff
 // with NWAVES waves, one 1 KiB slice (one direct-to-LDS copy) at a time, so
 // that the copies of a tile can be spread over the work of a loop iteration.
 // The per-lane byte offsets of the slices are computed once; a full tile then
-// needs only scalar address arithmetic per copy.  Rows at or beyond N (a
-// ragged last tile) are clamped to row N - 1.  Callers wait (vmcnt(0)) and
-// synchronise before any wave reads the tile.
+// needs two vector operations per copy.  Rows at or beyond N (a ragged last
+// tile) are clamped to row N - 1.  Callers wait (vmcnt(0)) and synchronise
+// before any wave reads the tile.
 template <int NROWS, int NWAVES>
 struct TileCopier {
     static constexpr int PER_WAVE = NROWS * ROWB / NWAVES;
@@ -185,19 +185,20 @@ struct TileCopier {
             voff[j] = (uint32_t)(row * ROWB + chunk * 16);
         }
     }
-    // slice j of rows [r0, r0 + NROWS) of src into the LDS tile at byte lds_tile
+    // Slice j of rows [r0, r0 + NROWS) of src into the LDS tile at byte
+    // lds_tile.  Branch-free: the base row r0 and the lane's row are both
+    // clamped into [0, N), which also turns a tile that starts at or beyond N
+    // into a harmless copy of row N - 1.  (A fast path for full tiles behind
+    // a branch measured slower: the branches split the loops that issue these
+    // copies into small blocks.)
     __device__ __forceinline__ void copy(int j, const e16_t* src, int r0, int N,
                                          uint32_t lds_tile) const {
-        const uint32_t lds = lds_tile + lds_wave + j * 1024;
-        if (r0 + NROWS <= N) {
-            lds_copy16_sbase(src + (long long)r0 * D, voff[j], lds);
-        } else {
-            int g = r0 + rowj[j];
-            g = g < N ? g : N - 1;
-            lds_copy16(reinterpret_cast<const unsigned char*>(src + (long long)g * D) +
-                           (voff[j] & (ROWB - 1)),
-                       lds);
-        }
+        const int rb = r0 < N ? r0 : N - 1;
+        const int lim = N - 1 - rb;
+        const int row = rowj[j] < lim ? rowj[j] : lim;
+        lds_copy16_sbase(src + (long long)rb * D,
+                         (uint32_t)(row * ROWB) + (voff[j] & (ROWB - 1)),
+                         lds_tile + lds_wave + j * 1024);
     }
 };
 

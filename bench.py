@@ -40,7 +40,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="h32_n8192_d128_bf16",
+                   choices=["h8_n1024_d64_bf16", "h32_n8192_d128_bf16",
+                            "b4_h16_n4000_d128_bf16_q4", "h8_n32768_d128_bf16"])
     p.add_argument("--causal", action="store_true", help="primary line is the causal run")
     p.add_argument("--no-extra", action="store_true", help="skip the second causal mode")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -198,7 +200,7 @@ def cpu_baseline(wl, causal: bool, budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py: the benchmark runs on one GPU only (--gpus {args.gpus} requested); "
               "heads shard across GPUs with no communication, see the design notes.", file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -5,14 +5,15 @@ tensors from a seeded PCG64 generator and quantises them to bfloat16 with
 round-to-nearest-even on the integer bit pattern.  The GPU receives exactly the
 bf16 bits produced here; the oracle receives the same values upcast to float64.
 
-Workloads (the five problem sizes of the FlashAttention-2 backward study):
-  c1  B=1 H=1  N=48    d=16  fp32  non-causal and causal, oracle O/L
-  c2  B=1 H=8  N=1024  d=64  bf16  non-causal
-  c3  B=1 H=32 N=8192  d=128 bf16  non-causal and causal
-  c4  B=4 H=16 N=4000  d=128 bf16  causal, Q multiplied by 4 after drawing
-  c5  B=1 H=8  N=32768 d=128 bf16  causal
-Q, K, V, dO are drawn in that order from one generator per workload with
-seed c1=0 .. c5=4; the scale is 1/sqrt(d).
+Workloads (the five problem sizes of the FlashAttention-2 backward study),
+keyed by their shapes:
+  n48_d16_fp32               B=1 H=1  N=48    d=16  fp32  non-causal and causal
+  h8_n1024_d64_bf16          B=1 H=8  N=1024  d=64  bf16  non-causal
+  h32_n8192_d128_bf16        B=1 H=32 N=8192  d=128 bf16  non-causal and causal
+  b4_h16_n4000_d128_bf16_q4  B=4 H=16 N=4000  d=128 bf16  causal, Q x 4 after drawing
+  h8_n32768_d128_bf16        B=1 H=8  N=32768 d=128 bf16  causal
+Q, K, V, dO are drawn in that order from one generator per workload, with
+seeds 0 .. 4 in the order listed; the scale is 1/sqrt(d).
 """
 from __future__ import annotations
 
@@ -44,13 +45,13 @@ class Workload:
         return 0.5 * f if causal else f
 
 
-WORKLOADS = {
-    "c1": Workload("c1", 1, 1, 48, 16, "fp32", (False, True), 0),
-    "c2": Workload("c2", 1, 8, 1024, 64, "bf16", (False,), 1),
-    "c3": Workload("c3", 1, 32, 8192, 128, "bf16", (False, True), 2),
-    "c4": Workload("c4", 4, 16, 4000, 128, "bf16", (True,), 3, q_mult=4.0),
-    "c5": Workload("c5", 1, 8, 32768, 128, "bf16", (True,), 4),
-}
+WORKLOADS = {w.name: w for w in (
+    Workload("n48_d16_fp32", 1, 1, 48, 16, "fp32", (False, True), 0),
+    Workload("h8_n1024_d64_bf16", 1, 8, 1024, 64, "bf16", (False,), 1),
+    Workload("h32_n8192_d128_bf16", 1, 32, 8192, 128, "bf16", (False, True), 2),
+    Workload("b4_h16_n4000_d128_bf16_q4", 4, 16, 4000, 128, "bf16", (True,), 3, q_mult=4.0),
+    Workload("h8_n32768_d128_bf16", 1, 8, 32768, 128, "bf16", (True,), 4),
+)}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -27,59 +27,59 @@ def _assert_grads(errs, tol, what):
         assert errs[n] <= tol, f"{what}: {n} rel err {errs[n]:.3e} > {tol}"
 
 
-# ---------------------------------------------------------------- workload c1
+# ---------------------------------------------------------------- workload n48_d16_fp32
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_c1_fp32_oracle_O_L(causal):
     """N=48, d=16, fp32: O and L from the oracle forward feed the GPU backward."""
-    wl = si.WORKLOADS["c1"]
-    gu.note(f"case c1 fp32 causal={causal} (oracle O, L)")
+    wl = si.WORKLOADS["n48_d16_fp32"]
+    gu.note(f"case n48_d16_fp32 fp32 causal={causal} (oracle O, L)")
     inp = si.draw(wl)
     O, L = oracle.attn_fwd(inp.Q, inp.K, inp.V, wl.scale, causal)
     out = gu.run_gpu(inp, causal, O=O.astype(np.float32), L=L)
     errs = gu.compare_full(inp, causal, out)
     gu.note(f"  errs {errs}")
-    _assert_grads(errs, gu.TOL["fp32"], "c1")
+    _assert_grads(errs, gu.TOL["fp32"], "n48_d16_fp32")
     assert errs["D"] <= 1e-5
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_c1_fp32_end_to_end(causal):
-    wl = si.WORKLOADS["c1"]
-    gu.note(f"case c1 fp32 causal={causal} (GPU forward)")
+    wl = si.WORKLOADS["n48_d16_fp32"]
+    gu.note(f"case n48_d16_fp32 fp32 causal={causal} (GPU forward)")
     inp = si.draw(wl)
     out = gu.run_gpu(inp, causal)
     errs = gu.compare_full(inp, causal, out)
     gu.note(f"  errs {errs}")
-    _assert_grads(errs, gu.TOL["fp32"], "c1 e2e")
+    _assert_grads(errs, gu.TOL["fp32"], "n48_d16_fp32 e2e")
     assert errs["o"] <= 1e-5 and errs["L"] <= 1e-5
 
 
-# ---------------------------------------------------------------- workload c2
+# ---------------------------------------------------------------- workload h8_n1024_d64_bf16
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_c2_bf16_full(causal):
     """B=1, H=8, N=1024, d=64 bf16 (the workload is non-causal; causal added)."""
-    wl = si.WORKLOADS["c2"]
-    gu.note(f"case c2 bf16 causal={causal}")
+    wl = si.WORKLOADS["h8_n1024_d64_bf16"]
+    gu.note(f"case h8_n1024_d64_bf16 bf16 causal={causal}")
     inp = si.draw(wl)
     out = gu.run_gpu(inp, causal)
     errs = gu.compare_full(inp, causal, out)
     gu.note(f"  errs {errs}")
-    _assert_grads(errs, gu.TOL["bf16"], "c2")
+    _assert_grads(errs, gu.TOL["bf16"], "h8_n1024_d64_bf16")
     assert errs["o"] <= 2e-2 and errs["L"] <= 1e-3
 
 
 def test_c2_isolated_backward():
     """The oracle's O (rounded to bf16) and L feed the GPU backward."""
-    wl = si.WORKLOADS["c2"]
-    gu.note("case c2 bf16 isolated backward")
+    wl = si.WORKLOADS["h8_n1024_d64_bf16"]
+    gu.note("case h8_n1024_d64_bf16 bf16 isolated backward")
     inp = si.draw(wl)
     O, L = oracle.attn_fwd(inp.Q, inp.K, inp.V, wl.scale, False)
     out = gu.run_gpu(inp, False, O=O.astype(np.float32), L=L)
     errs = gu.compare_full(inp, False, out)
     gu.note(f"  errs {errs}")
-    _assert_grads(errs, gu.TOL["bf16"], "c2 isolated")
+    _assert_grads(errs, gu.TOL["bf16"], "h8_n1024_d64_bf16 isolated")
 
 
 # ------------------------------------------------------------ edge shapes
@@ -188,15 +188,15 @@ def test_split_passes_equal_fa_bwd(causal):
 
 # ------------------------------------------------------ full-size workloads
 
-FULL = [("c3", False, "bf16"), ("c3", True, "bf16"), ("c4", True, "bf16"), ("c5", True, "bf16"),
-        ("c3", False, "fp16")]
-HEADS = {"c3": [(0, 0), (0, 31)], "c4": [(0, 0), (3, 15)], "c5": [(0, 5)]}
+FULL = [("h32_n8192_d128_bf16", False, "bf16"), ("h32_n8192_d128_bf16", True, "bf16"), ("b4_h16_n4000_d128_bf16_q4", True, "bf16"), ("h8_n32768_d128_bf16", True, "bf16"),
+        ("h32_n8192_d128_bf16", False, "fp16")]
+HEADS = {"h32_n8192_d128_bf16": [(0, 0), (0, 31)], "b4_h16_n4000_d128_bf16_q4": [(0, 0), (3, 15)], "h8_n32768_d128_bf16": [(0, 5)]}
 
 
 @pytest.mark.parametrize("name,causal,dtype", FULL,
                          ids=[f"{n}-{'causal' if c else 'full'}-{dt}" for n, c, dt in FULL])
 def test_full_size_sampled(name, causal, dtype):
-    """Full problem sizes (the c3 shape also in fp16, the same contract)."""
+    """Full problem sizes (the h32_n8192_d128_bf16 shape also in fp16, the same contract)."""
     wl = si.WORKLOADS[name]
     gu.note(f"case {name} B={wl.B} H={wl.H} N={wl.N} d={wl.d} causal={causal} {dtype}: drawing")
     inp = si.draw(wl, dtype=dtype)

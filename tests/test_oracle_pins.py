@@ -156,8 +156,8 @@ def test_D_identity(causal):
 
 
 def _tiled_cases():
-    c1 = si.draw(si.WORKLOADS["c1"])
-    yield "c1", c1.Q, c1.K, c1.V, c1.dO, 16, 12
+    w = si.draw(si.WORKLOADS["n48_d16_fp32"])
+    yield "n48_d16_fp32", w.Q, w.K, w.V, w.dO, 16, 12
     big = si.draw_custom(1, 2, 50, 16, "fp32", seed=7, q_mult=4.0)
     yield "ragged_q4", big.Q, big.K, big.V, big.dO, 16, 12
     tiny = si.draw_custom(1, 1, 5, 8, "fp32", seed=8)
