@@ -147,8 +147,11 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     split = {name: [e[j].elapsed_time(e[j + 1]) for e in evs]
              for j, name in enumerate(("fa_bwd_preprocess", "fa_bwd_dq", "fa_bwd_dkdv",
                                        "fa_bwd_convert_dq"))}
+    per_step = [e[0].elapsed_time(e[4]) for e in evs]
     return {
         "ms_per_step": total_ms / steps,
+        "step_ms": {"median": round(statistics.median(per_step), 4),
+                    "min": round(min(per_step), 4)},
         "wall_ms_per_step": 1e3 * wall / steps,
         "kernel_ms": {k: statistics.fmean(v) for k, v in split.items()},
         "kernel_ms_min": {k: min(v) for k, v in split.items()},
@@ -192,9 +195,19 @@ def cpu_baseline(wl, causal: bool, budget_s: float):
         elapsed += time.perf_counter() - t0
         heads += 1
     flop = 10.0 * wl.N * wl.N * wl.d * (0.5 if causal else 1.0) * heads
+    model = "unknown CPU"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": flop / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} head(s) of N={wl.N}, d={wl.d} ({'causal' if causal else 'non-causal'}), "
-                      f"fp64 backward by definition, {elapsed:.1f} s"}
+                      f"fp64 backward by definition, {elapsed:.1f} s",
+            # the host the oracle ran on (hosts differ from one run to the next)
+            "host": f"{len(os.sched_getaffinity(0))} CPUs usable of {os.cpu_count()}, {model}"}
 
 
 def main():
@@ -260,6 +273,7 @@ def main():
                    "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "causal": args.causal,
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(prim["pct_peak"], 2),
+        "step_ms": prim["step_ms"],
         "split_ms": {k: round(v, 4) for k, v in prim["kernel_ms"].items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": kd["achieved"],
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kd["frac"],
@@ -273,6 +287,7 @@ def main():
         other = results[not args.causal]
         line["causal" if not args.causal else "non_causal"] = {
             "value": round(other["tflops"], 3), "ms_per_step": round(other["ms_per_step"], 4),
+            "step_ms": other["step_ms"],
             "pct_bf16_peak": round(other["pct_peak"], 2),
             "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
             "kernels": other["kernels"], "forward": other["forward"]}
