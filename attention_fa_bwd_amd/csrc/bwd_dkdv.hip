@@ -108,6 +108,15 @@ __device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP, 
     pd = E::pack2(d[0], d[1]);
 }
 
+// dS of elements r, r + 1 from P (already exponentiated, in S) and dP, and
+// both pairs packed.
+template <typename E>
+__device__ __forceinline__ void ds_finish(const f32x16_t& P, const f32x16_t& dP, int r,
+                                          uint32_t& pp, uint32_t& pd) {
+    pp = E::pack2(P[r], P[r + 1]);
+    pd = E::pack2(P[r] * dP[r], P[r + 1] * dP[r + 1]);
+}
+
 // Score role on a diagonal tile (causal mask applied element by element):
 // block by block, no interleaving -- two such tiles per workgroup, and the
 // mask needs registers the interleaved order does not have to spare.
@@ -188,18 +197,29 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         dP0 = E::mma(ag[i % 3], vt[i], dP0);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // Block 0's P and dS under block 1's products, software-pipelined so that
+    // no result is used by the very next instruction: after the first pair
+    // of products all sixteen scores go to exp2 units; step k then takes the
+    // exponentials of pair k and finishes (dS, packing) pair k - 1.
     uint32_t pk[8], dk[8];
 #pragma unroll
     for (int i = 8; i < 16; ++i) {
+        const int k = i - 8;
         if (i + 2 < 16) {
             aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
             ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
         }
         S1 = E::mma(aq[i % 3], kt[i - 8], S1);
         dP1 = E::mma(ag[i % 3], vt[i - 8], dP1);
-        pds_pair<E, false>(S0, dP0, 2 * (i - 8), sc, 0, 0, pk[i - 8], dk[i - 8]);
+        if (k == 0)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S0[e] *= sc;
+        S0[2 * k] = __builtin_amdgcn_exp2f(S0[2 * k]);
+        S0[2 * k + 1] = __builtin_amdgcn_exp2f(S0[2 * k + 1]);
+        if (k >= 1) ds_finish<E>(S0, dP0, 2 * k - 2, pk[k - 1], dk[k - 1]);
         __builtin_amdgcn_sched_barrier(0);
     }
+    ds_finish<E>(S0, dP0, 14, pk[7], dk[7]);
     // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -207,8 +227,16 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
         *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
     }
+    // block 1's P and dS with nothing else to overlap: grouped by operation
+    // so that dependent instructions stand sixteen apart
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pds_pair<E, false>(S1, dP1, 2 * j, sc, 0, 0, pk[j], dk[j]);
+    for (int e = 0; e < 16; ++e) S1[e] *= sc;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S1[e] = __builtin_amdgcn_exp2f(S1[e]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ds_finish<E>(S1, dP1, 2 * j, pk[j], dk[j]);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
         const int slab = ((2 + hh) * 4 + s) * SLAB + l * 16;
@@ -377,8 +405,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     for (int p = 0; p <= ntiles; ++p) {
         // copies of tile p + 1 first: they need the whole phase to land.  In
         // the last two phases the buffer they fill is read by no one; they
-        // are issued all the same (rows clamped into range), which keeps the
-        // loop free of branches around them -- measurably faster.
+        // are issued all the same (rows clamped into range) rather than
+        // behind a branch.
         const int qn = q_begin + (p + 1) * BR;
         const uint32_t lq = lds0 + OFF_Q + ((p + 1) % 3) * TILE;
 #pragma unroll

@@ -71,6 +71,14 @@ __device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& d
     return E::pack2(d[0], d[1]);
 }
 
+// dS of elements r, r + 1 from P (already exponentiated, in S) and dP,
+// packed.
+template <typename E>
+__device__ __forceinline__ uint32_t ds_finish(const f32x16_t& P, const f32x16_t& dP, int r,
+                                              float Dq) {
+    return E::pack2(P[r] * (dP[r] - Dq), P[r + 1] * (dP[r + 1] - Dq));
+}
+
 // Score role: dS of key block k0 for this wave's 32 queries, stored as slabs
 // (t = 2 mb + hh, query group s), lane-ordered 16 bytes.  Operand reads run
 // two MFMA pairs ahead; outside masked blocks the S^T/dP^T products of key
@@ -128,21 +136,40 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
         dP0 = E::mma(av[i % 3], gt[i], dP0);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // Half 0's dS under half 1's products, software-pipelined so that no
+    // result is used by the very next instruction: after the first pair of
+    // products all sixteen scores go to exp2 units; step k then takes the
+    // exponentials of pair k and finishes pair k - 1.
     uint32_t pk[8];
 #pragma unroll
     for (int i = 8; i < 16; ++i) {
+        const int k = i - 8;
         if (i + 2 < 16) {
             ak[(i + 2) % 3] = lds_b128(sK + opoff(i + 2));
             av[(i + 2) % 3] = lds_b128(sV + opoff(i + 2));
         }
         S1 = E::mma(ak[i % 3], qt[i - 8], S1);
         dP1 = E::mma(av[i % 3], gt[i - 8], dP1);
-        pk[i - 8] = ds_pair<E, false, CAUSAL>(S0, dP0, 2 * (i - 8), sc, Lq, Dq, 0, q, N);
+        if (k == 0)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) S0[e] = __builtin_fmaf(S0[e], sc, -Lq);
+        S0[2 * k] = __builtin_amdgcn_exp2f(S0[2 * k]);
+        S0[2 * k + 1] = __builtin_amdgcn_exp2f(S0[2 * k + 1]);
+        if (k >= 1) pk[k - 1] = ds_finish<E>(S0, dP0, 2 * k - 2, Dq);
         __builtin_amdgcn_sched_barrier(0);
     }
+    pk[7] = ds_finish<E>(S0, dP0, 14, Dq);
     store(0, pk);
+    // half 1's dS with nothing else to overlap: grouped by operation so that
+    // dependent instructions stand sixteen apart
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pk[j] = ds_pair<E, false, CAUSAL>(S1, dP1, 2 * j, sc, Lq, Dq, 0, q, N);
+    for (int e = 0; e < 16; ++e) S1[e] = __builtin_fmaf(S1[e], sc, -Lq);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) S1[e] = __builtin_amdgcn_exp2f(S1[e]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pk[j] = ds_finish<E>(S1, dP1, 2 * j, Dq);
     store(1, pk);
 }
 
@@ -259,8 +286,8 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         // copies of block p + 2 first; block p + 1's (issued one phase ago)
         // must have landed by the barrier, these may stay in flight.  Past
         // the last block the buffers they fill are read by no one; they are
-        // issued all the same (rows clamped into range), which keeps the
-        // products free of branches around them.
+        // issued all the same (rows clamped into range), so that no branch
+        // splits the products they are spread over.
         const int kn = (p + 2) * BK;
         const uint32_t lk = lds0 + OFF_K + ((p + 2) % NKB) * TILE;
         const uint32_t lv = lds0 + OFF_V + ((p + 2) % NVB) * TILE;

@@ -167,9 +167,11 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
                     if (key >= N || (CAUSAL && key > q)) s2[e] = -INFINITY;
                 }
             }
-            float bm = s2[0];
+            // block maximum as four interleaved chains (exact in any order)
+            float m4[4] = {s2[0], s2[1], s2[2], s2[3]};
 #pragma unroll
-            for (int e = 1; e < 32; ++e) bm = fmaxf(bm, s2[e]);
+            for (int e = 4; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], s2[e]);
+            float bm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
             bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
             const bool rebase = bm > mu + kLazy;
             if (__ballot(rebase)) {
@@ -181,12 +183,20 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
+            // terms grouped by operation, the denominator summed in four
+            // interleaved partial sums, so that no result feeds the very next
+            // instruction
             float p[32];
 #pragma unroll
-            for (int e = 0; e < 32; ++e) {
-                p[e] = __builtin_amdgcn_exp2f(s2[e] - mu);
-                lsum += p[e];
-            }
+            for (int e = 0; e < 32; ++e) p[e] = s2[e] - mu;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e]);
+            __builtin_amdgcn_sched_barrier(0);
+            float l4[4] = {p[0], p[1], p[2], p[3]};
+#pragma unroll
+            for (int e = 4; e < 32; ++e) l4[e & 3] += p[e];
+            lsum += (l4[0] + l4[1]) + (l4[2] + l4[3]);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 pb[t] = as_v16x8(make_uint4(E::pack2(p[8 * t], p[8 * t + 1]),

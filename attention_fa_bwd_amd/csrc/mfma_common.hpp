@@ -186,11 +186,10 @@ struct TileCopier {
         }
     }
     // Slice j of rows [r0, r0 + NROWS) of src into the LDS tile at byte
-    // lds_tile.  Branch-free: the base row r0 and the lane's row are both
-    // clamped into [0, N), which also turns a tile that starts at or beyond N
-    // into a harmless copy of row N - 1.  (A fast path for full tiles behind
-    // a branch measured slower: the branches split the loops that issue these
-    // copies into small blocks.)
+    // lds_tile.  Branch-free, so that a copy can sit anywhere in a stretch of
+    // products without splitting it into separate blocks: the base row r0 and
+    // the lane's row are both clamped into [0, N), which also turns a tile
+    // that starts at or beyond N into a harmless copy of row N - 1.
     __device__ __forceinline__ void copy(int j, const e16_t* src, int r0, int N,
                                          uint32_t lds_tile) const {
         const int rb = r0 < N ? r0 : N - 1;
