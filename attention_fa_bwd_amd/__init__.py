@@ -13,10 +13,10 @@ import os
 import torch
 
 __all__ = [
-    "FA_DTYPE_F32", "FA_DTYPE_BF16", "FAError", "lib_path", "load",
-    "fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
+    "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FAError", "lib_path", "load",
+    "fa_fwd_lse", "fa_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
     "fa_bwd_convert_dq", "fa_strerror",
-    "forward", "backward",
+    "forward", "lse", "backward",
 ]
 
 FA_DTYPE_F32 = 0
@@ -32,6 +32,7 @@ _lib = None
 _vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 _SIGS = {
     "fa_fwd_lse": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
+    "fa_lse": [_i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_preprocess": [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp],
     "fa_bwd": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_dkdv": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
@@ -123,6 +124,14 @@ def fa_fwd_lse(q, k, v, o, L, scale: float, causal: bool, stream=None) -> None:
     _check("fa_fwd_lse", rc)
 
 
+def fa_lse(q, k, L, scale: float, causal: bool, stream=None) -> None:
+    B, H, N, d = _shape(q)
+    dt = _dtype_code(q)
+    rc = load().fa_lse(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(L, torch.float32),
+                       B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    _check("fa_lse", rc)
+
+
 def fa_bwd_preprocess(o, do, D, dq_accum, stream=None) -> None:
     B, H, N, d = _shape(o)
     dt = _dtype_code(o)
@@ -177,6 +186,14 @@ def forward(q, k, v, scale: float, causal: bool, stream=None):
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     fa_fwd_lse(q, k, v, o, L, scale, causal, stream)
     return o, L
+
+
+def lse(q, k, scale: float, causal: bool, stream=None):
+    """L alone (allocates it): for a backward whose forward did not keep L."""
+    B, H, N, d = _shape(q)
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_lse(q, k, L, scale, causal, stream)
+    return L
 
 
 def backward(q, k, v, o, do, L, scale: float, causal: bool, stream=None, workspace=None):

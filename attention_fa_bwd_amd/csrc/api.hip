@@ -64,6 +64,18 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V, void* O, 
                                      (hipStream_t)stream));
 }
 
+int fa_lse(int dtype, const void* Q, const void* K, float* L, int B, int H, int N, int d,
+           float scale, int causal, void* stream) {
+    int rc = check(dtype, B, H, N, d, {Q, K, L});
+    if (rc != FA_OK) return rc;
+    if ((rc = device_ready()) != FA_OK) return rc;
+    const fa::Shape s{B, H, N, d};
+    if (matrix_core(dtype, d))
+        return hip_status(fa::launch_lse_d128(dtype, Q, K, L, s, scale, causal != 0,
+                                              (hipStream_t)stream));
+    return hip_status(fa::launch_lse(dtype, Q, K, L, s, scale, causal != 0, (hipStream_t)stream));
+}
+
 int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D, float* dq_accum,
                       int B, int H, int N, int d, void* stream) {
     int rc = check(dtype, B, H, N, d, {O, dO, D, dq_accum});

@@ -12,12 +12,14 @@
 // accumulator, so a K/V row read from LDS is a 4-address broadcast.  Key blocks
 // of 32 rows are staged in LDS as fp32.  Under the causal mask the key loop
 // stops after the block's last row (whole tiles above the diagonal are never
-// visited, FA2 chapter 16 sec 16.8 item 2).
+// visited, FA2 chapter 16 sec 16.8 item 2).  Without O (WITH_O false) the
+// kernel only keeps m and l: the pass that recomputes L when the forward did
+// not store it (FA2 chapter 16 sec 16.4).
 #include "launch.hpp"
 
 namespace fa {
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool WITH_O>
 __global__ __launch_bounds__(256) void fwd_simt_kernel(const T* __restrict__ Q,
                                                        const T* __restrict__ K,
                                                        const T* __restrict__ V,
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(const T* __restrict__ Q,
         for (int e = threadIdx.x; e < BC * D; e += 256) {
             const int c = e / D, k = e % D, j = k0 + c;
             sK[c][k] = j < N ? to_f32(Kh[(long long)j * D + k]) : 0.f;
-            sV[c][k] = j < N ? to_f32(Vh[(long long)j * D + k]) : 0.f;
+            if (WITH_O) sV[c][k] = j < N ? to_f32(Vh[(long long)j * D + k]) : 0.f;
         }
         __syncthreads();
         float s[BC];
@@ -70,55 +72,68 @@ __global__ __launch_bounds__(256) void fwd_simt_kernel(const T* __restrict__ Q,
         if (mn == -INFINITY) continue;  // nothing visible yet for this row
         const float alpha = (m == -INFINITY) ? 0.f : expf(m - mn);
         l *= alpha;
+        if (WITH_O)
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) o[i] *= alpha;
+            for (int i = 0; i < CPT; ++i) o[i] *= alpha;
 #pragma unroll
         for (int c = 0; c < BC; ++c) {
             const float p = (s[c] == -INFINITY) ? 0.f : expf(s[c] - mn);
             l += p;
+            if (WITH_O)
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) o[i] = fmaf(p, sV[c][t + 4 * i], o[i]);
+                for (int i = 0; i < CPT; ++i) o[i] = fmaf(p, sV[c][t + 4 * i], o[i]);
         }
         m = mn;
     }
     if (r < N) {
-        const float inv = 1.f / l;
+        if (WITH_O) {
+            const float inv = 1.f / l;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) O[head * N * D + (long long)r * D + t + 4 * i] = from_f32<T>(o[i] * inv);
+            for (int i = 0; i < CPT; ++i)
+                O[head * N * D + (long long)r * D + t + 4 * i] = from_f32<T>(o[i] * inv);
+        }
         if (t == 0) L[head * N + r] = m + logf(l);
     }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool WITH_O>
 static hipError_t fwd_t(const void* Q, const void* K, const void* V, void* O, float* L, Shape s,
                         float scale, bool causal, hipStream_t st) {
     dim3 grid((s.N + 63) / 64, s.H, s.B);
     if (causal)
-        hipLaunchKernelGGL((fwd_simt_kernel<T, D, true>), grid, dim3(256), 0, st, (const T*)Q,
-                           (const T*)K, (const T*)V, (T*)O, L, s.N, scale);
+        hipLaunchKernelGGL((fwd_simt_kernel<T, D, true, WITH_O>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, s.N, scale);
     else
-        hipLaunchKernelGGL((fwd_simt_kernel<T, D, false>), grid, dim3(256), 0, st, (const T*)Q,
-                           (const T*)K, (const T*)V, (T*)O, L, s.N, scale);
+        hipLaunchKernelGGL((fwd_simt_kernel<T, D, false, WITH_O>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (T*)O, L, s.N, scale);
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool WITH_O>
 static hipError_t fwd_d(const void* Q, const void* K, const void* V, void* O, float* L, Shape s,
                         float scale, bool causal, hipStream_t st) {
     switch (s.d) {
-        case 16: return fwd_t<T, 16>(Q, K, V, O, L, s, scale, causal, st);
-        case 32: return fwd_t<T, 32>(Q, K, V, O, L, s, scale, causal, st);
-        case 64: return fwd_t<T, 64>(Q, K, V, O, L, s, scale, causal, st);
-        case 128: return fwd_t<T, 128>(Q, K, V, O, L, s, scale, causal, st);
+        case 16: return fwd_t<T, 16, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
+        case 32: return fwd_t<T, 32, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
+        case 64: return fwd_t<T, 64, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
+        case 128: return fwd_t<T, 128, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, void* O, float* L,
                       Shape s, float scale, bool causal, hipStream_t st) {
-    return dtype == DT_BF16  ? fwd_d<bf16_t>(Q, K, V, O, L, s, scale, causal, st)
-           : dtype == DT_F16 ? fwd_d<f16_t>(Q, K, V, O, L, s, scale, causal, st)
-                             : fwd_d<float>(Q, K, V, O, L, s, scale, causal, st);
+    return dtype == DT_BF16  ? fwd_d<bf16_t, true>(Q, K, V, O, L, s, scale, causal, st)
+           : dtype == DT_F16 ? fwd_d<f16_t, true>(Q, K, V, O, L, s, scale, causal, st)
+                             : fwd_d<float, true>(Q, K, V, O, L, s, scale, causal, st);
+}
+
+// L alone (no O); V is never read, K stands in for it.
+hipError_t launch_lse(int dtype, const void* Q, const void* K, float* L, Shape s, float scale,
+                      bool causal, hipStream_t st) {
+    return dtype == DT_BF16  ? fwd_d<bf16_t, false>(Q, K, K, nullptr, L, s, scale, causal, st)
+           : dtype == DT_F16 ? fwd_d<f16_t, false>(Q, K, K, nullptr, L, s, scale, causal, st)
+                             : fwd_d<float, false>(Q, K, K, nullptr, L, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -24,6 +24,11 @@
 // loads); K rotates through three buffers, V through four (112 KiB).  Key rows
 // at or beyond N are staged as copies of row N - 1 and masked; query rows at
 // or beyond N are not stored.
+//
+// Without O (WITH_O false) the same kernel is the pass that recomputes L
+// when the forward did not store it (FA2 chapter 16 sec 16.4: the backward
+// then has to run the online softmax once more, a full sweep over K): no V
+// copies, no O^T products, only the running maximum and denominator.
 #include "launch.hpp"
 #include "mfma_common.hpp"
 
@@ -46,11 +51,12 @@ static_assert(LDS_BYTES == 112 * 1024, "LDS plan");
 constexpr float kLazy = 8.f;             // rebase threshold, log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <typename E, bool CAUSAL>
+template <typename E, bool CAUSAL, bool WITH_O>
 __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
     e16_t* __restrict__ O, float* __restrict__ Lg, int N, int nqb, float scale) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+    // without O only the K buffers are used (48 KiB): two workgroups fit a CU
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[WITH_O ? LDS_BYTES : OFF_V];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
     const int head = work / nqb;
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     for (int b = 0; b < SD; ++b) {
         if (b < nblk) {
             stage_rows<BK, NWAVE>(smem + OFF_K + b * TILE, Kh, b * BK, N, wave, l);
-            stage_rows<BK, NWAVE>(smem + OFF_V + b * TILE, Vh, b * BK, N, wave, l);
+            if (WITH_O) stage_rows<BK, NWAVE>(smem + OFF_V + b * TILE, Vh, b * BK, N, wave, l);
         }
     }
     const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
@@ -106,7 +112,9 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     v16x8_t pb[4];   // P^T of the previous block, 16-key step t = 2 mb + hh
     float mu = -1e30f, lsum = 0.f;
 
-    for (int j = 0; j <= nblk; ++j) {
+    // with O the last phase only adds block nblk - 1's O^T products
+    const int jend = WITH_O ? nblk : nblk - 1;
+    for (int j = 0; j <= jend; ++j) {
         // copies of block j + SD; past the last block the buffers they fill
         // are read by no one, and they are issued all the same (rows clamped
         // into range) to keep the loop free of branches around them
@@ -117,10 +125,10 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 #pragma unroll
             for (int s = 0; s < cp.SLICES; ++s) {
                 cp.copy(s, Kh, kn, N, lk);
-                cp.copy(s, Vh, kn, N, lv);
+                if (WITH_O) cp.copy(s, Vh, kn, N, lv);
             }
         }
-        const bool mf = j < nblk, pv = j >= 1;
+        const bool mf = j < nblk, pv = WITH_O && j >= 1;
         const unsigned char* sK = smem + OFF_K + (j % NKB) * TILE;
         const unsigned char* sV = smem + OFF_V + ((j + NVB - 1) % NVB) * TILE;
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
@@ -178,10 +186,11 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
                 const float alpha = rebase ? __builtin_amdgcn_exp2f(mu - bm) : 1.f;
                 mu = rebase ? bm : mu;
                 lsum *= alpha;
+                if (WITH_O)
 #pragma unroll
-                for (int db = 0; db < 4; ++db)
+                    for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+                        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
             // terms grouped by operation, the denominator summed in four
             // interleaved partial sums, so that no result feeds the very next
@@ -197,17 +206,18 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 #pragma unroll
             for (int e = 4; e < 32; ++e) l4[e & 3] += p[e];
             lsum += (l4[0] + l4[1]) + (l4[2] + l4[3]);
+            if (WITH_O)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                pb[t] = as_v16x8(make_uint4(E::pack2(p[8 * t], p[8 * t + 1]),
+                for (int t = 0; t < 4; ++t)
+                    pb[t] = as_v16x8(make_uint4(E::pack2(p[8 * t], p[8 * t + 1]),
                                              E::pack2(p[8 * t + 2], p[8 * t + 3]),
                                              E::pack2(p[8 * t + 4], p[8 * t + 5]),
                                              E::pack2(p[8 * t + 6], p[8 * t + 7])));
         }
         // block j + 1's copies (issued one phase ago) must have landed; this
         // phase's may stay in flight
-        if (j < nblk)
-            __builtin_amdgcn_s_waitcnt(kVmcnt4Lgkm0);
+        if (j < jend)
+            __builtin_amdgcn_s_waitcnt(WITH_O ? kVmcnt4Lgkm0 : kVmcnt2Lgkm0);
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -215,23 +225,25 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
     if (q < N) {
-        const float inv = 1.f / ltot;
-        e16_t* orow = O + hoff + (long long)q * D;
+        if (WITH_O) {
+            const float inv = 1.f / ltot;
+            e16_t* orow = O + hoff + (long long)q * D;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int r = 4 * a4;
-                uint2 v;
-                v.x = E::pack2(acc[db][r] * inv, acc[db][r + 1] * inv);
-                v.y = E::pack2(acc[db][r + 2] * inv, acc[db][r + 3] * inv);
-                *reinterpret_cast<uint2*>(orow + 32 * db + 8 * a4 + 4 * h) = v;
-            }
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int r = 4 * a4;
+                    uint2 v;
+                    v.x = E::pack2(acc[db][r] * inv, acc[db][r + 1] * inv);
+                    v.y = E::pack2(acc[db][r + 2] * inv, acc[db][r + 3] * inv);
+                    *reinterpret_cast<uint2*>(orow + 32 * db + 8 * a4 + 4 * h) = v;
+                }
+        }
         if (h == 0) Lg[(long long)head * N + q] = (mu + __builtin_log2f(ltot)) * kLn2;
     }
 }
 
-template <typename E>
+template <typename E, bool WITH_O>
 hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O, float* L,
                            Shape s, float scale, bool causal, hipStream_t st) {
     const int nqb = (s.N + BQ - 1) / BQ;
@@ -239,11 +251,11 @@ hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O,
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((fwd_mfma_kernel<E, true>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, true, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
                            nqb, scale);
     else
-        hipLaunchKernelGGL((fwd_mfma_kernel<E, false>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, false, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
                            nqb, scale);
     return hipGetLastError();
@@ -253,8 +265,16 @@ hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O,
 
 hipError_t launch_fwd_d128(int dtype, const void* Q, const void* K, const void* V, void* O,
                            float* L, Shape s, float scale, bool causal, hipStream_t st) {
-    return dtype == DT_F16 ? launch_fwd_mfma<F16E>(Q, K, V, O, L, s, scale, causal, st)
-                           : launch_fwd_mfma<Bf16E>(Q, K, V, O, L, s, scale, causal, st);
+    return dtype == DT_F16 ? launch_fwd_mfma<F16E, true>(Q, K, V, O, L, s, scale, causal, st)
+                           : launch_fwd_mfma<Bf16E, true>(Q, K, V, O, L, s, scale, causal, st);
+}
+
+// L alone (no O); V is never read, K stands in for it.
+hipError_t launch_lse_d128(int dtype, const void* Q, const void* K, float* L, Shape s,
+                           float scale, bool causal, hipStream_t st) {
+    return dtype == DT_F16
+               ? launch_fwd_mfma<F16E, false>(Q, K, K, nullptr, L, s, scale, causal, st)
+               : launch_fwd_mfma<Bf16E, false>(Q, K, K, nullptr, L, s, scale, causal, st);
 }
 
 }  // namespace fa

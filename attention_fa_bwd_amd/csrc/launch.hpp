@@ -20,6 +20,12 @@ hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, vo
 hipError_t launch_fwd_d128(int dtype, const void* Q, const void* K, const void* V, void* O,
                            float* L, Shape s, float scale, bool causal, hipStream_t st);
 
+// L alone, by the same two forward kernels without V and O.
+hipError_t launch_lse(int dtype, const void* Q, const void* K, float* L, Shape s, float scale,
+                      bool causal, hipStream_t st);
+hipError_t launch_lse_d128(int dtype, const void* Q, const void* K, float* L, Shape s,
+                           float scale, bool causal, hipStream_t st);
+
 // Vector-ALU backward (fp32 FMA): every dtype and head dim.
 hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* V,
                            const void* dO, const float* L, const float* D, float* dq_accum,

@@ -44,6 +44,7 @@ constexpr int kLgkmOnly = 0xC07F;
 // scalar traffic drained (vmcnt 8, expcnt 7, lgkmcnt 0).
 constexpr int kVmcnt8Lgkm0 = 0x0078;
 constexpr int kVmcnt4Lgkm0 = 0x0074;
+constexpr int kVmcnt2Lgkm0 = 0x0072;
 constexpr int D = 128;       // head dim of the matrix-core kernels
 constexpr int ROWB = D * 2;  // bytes per 16-bit row of Q, K, V, dO
 

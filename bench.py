@@ -179,6 +179,26 @@ def forward_time(wl, causal: bool, inputs, reps: int = 5):
     return a.elapsed_time(b) / reps
 
 
+def lse_time(wl, causal: bool, inputs, reps: int = 5):
+    """Time of fa_lse alone (L recomputed when the forward did not keep it;
+    not part of a step): HIP events around `reps` calls after one warm-up."""
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    q, k = inputs
+    L = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    fa.fa_lse(q, k, L, wl.scale, causal, stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fa.fa_lse(q, k, L, wl.scale, causal, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(wl, causal: bool, budget_s: float):
     """The oracle's full backward (by definition) on a bounded sample of heads."""
     import numpy as np
@@ -250,6 +270,10 @@ def main():
         ffl = 0.4 * flops  # 4·B·H·N²·d (×½ causal)
         r["forward"] = {"ms": round(fms, 4), "tflops": round(ffl / (fms * 1e-3) / 1e12, 3),
                         "bwd_over_fwd_time": round(r["ms_per_step"] / fms, 3)}
+        lms = lse_time(wl, causal, (up["Q"], up["K"]))
+        lfl = 0.2 * flops  # S only: 2·B·H·N²·d (×½ causal)
+        r["recompute_L"] = {"ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 3),
+                            "step_ms_with_it": round(r["ms_per_step"] + lms, 4)}
         results[causal] = r
         del o, L
     prim = results[args.causal]
@@ -282,6 +306,7 @@ def main():
                      "avg_launch_ms": kd["avg_launch_ms"]},
         "kernels": prim["kernels"],
         "forward": prim["forward"],
+        "recompute_L": prim["recompute_L"],
     }
     if len(results) > 1:
         other = results[not args.causal]
@@ -290,7 +315,8 @@ def main():
             "step_ms": other["step_ms"],
             "pct_bf16_peak": round(other["pct_peak"], 2),
             "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
-            "kernels": other["kernels"], "forward": other["forward"]}
+            "kernels": other["kernels"], "forward": other["forward"],
+            "recompute_L": other["recompute_L"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
     else:

@@ -79,6 +79,19 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V,
                void* stream);
 
 /*
+ * fa_lse -- the logsumexp L alone, for a backward whose forward did not store
+ * it.  FA2 chapter 16 sec 16.4 names the cost: the online softmax has to run
+ * once more, a full sweep over K (the chapter's closing exercise asks for
+ * it).  The same query-outer sweep as fa_fwd_lse with V and O left out: the
+ * running maximum m and denominator l per row, L = m + log l (natural log),
+ * bitwise the same L as fa_fwd_lse on the same inputs.
+ *   in : Q, K [B,H,N,d] dtype
+ *   out: L [B,H,N] fp32
+ */
+int fa_lse(int dtype, const void* Q, const void* K, float* L,
+           int B, int H, int N, int d, float scale, int causal, void* stream);
+
+/*
  * fa_bwd_preprocess -- D_i = sum_k O_ik dO_ik with fp32 accumulation (FA2
  * chapter 16 sec 16.1, the identity D_i = dO_i . O_i, and sec 16.8 item 1:
  * computed once before the main loop), and dq_accum := 0 so that the main

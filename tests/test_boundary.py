@@ -22,15 +22,16 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = fa.load()
     names = _declared()
-    assert {"fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq",
-            "fa_strerror"} <= set(names)
+    assert {"fa_fwd_lse", "fa_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq",
+            "fa_bwd_dkdv", "fa_bwd_dq", "fa_strerror"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_binding_has_same_names():
-    for n in ("fa_fwd_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq", "fa_strerror"):
-        assert callable(getattr(fa, n))
+    for n in _declared():
+        if n != "fa_last_hip_error":   # read by the binding's error path, not exposed
+            assert callable(getattr(fa, n)), n
 
 
 def test_strerror():
@@ -61,6 +62,9 @@ def test_invalid_arguments_rejected_before_device_work():
     assert _bwd(lib, B=60000, H=60000, N=60000, d=128) == fa.FA_EINVAL   # > 2^40 elements
     p = ALIGNED
     assert lib.fa_fwd_lse(1, p, p, None, p, p, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_lse(1, p, p, None, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_lse(2, p, p + 8, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL   # misaligned
+    assert lib.fa_lse(5, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
     assert lib.fa_bwd_preprocess(1, p, p, p, None, 1, 1, 8, 64, None) == fa.FA_EINVAL
     assert lib.fa_bwd_convert_dq(0, None, p, 1, 1, 8, 64, 0.1, None) == fa.FA_EINVAL
 
@@ -71,6 +75,7 @@ def test_unsupported_head_dim(d):
     p = ALIGNED
     assert _bwd(lib, d=d) == fa.FA_EUNSUPPORTED
     assert lib.fa_fwd_lse(0, p, p, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_lse(1, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_bwd_preprocess(1, p, p, p, p, 1, 1, 8, d, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_bwd_convert_dq(1, p, p, 1, 1, 8, d, 0.1, None) == fa.FA_EUNSUPPORTED
 

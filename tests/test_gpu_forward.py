@@ -1,5 +1,5 @@
-"""GPU parity of the forward (fa_fwd_lse): O and L against the oracle's plain
-definition, element by element.
+"""GPU parity of the forward (fa_fwd_lse) and of L alone (fa_lse): O and L
+against the oracle's plain definition, element by element.
 
 bf16 and fp16 with d = 128 run the matrix-core kernel (lazy rebase of the running
 maximum); the other cases run the vector-ALU kernel.  Tolerances: O within the
@@ -7,6 +7,7 @@ element type's bar (max |err| / max |ref|), L (natural log, fp32) within 1e-4
 absolute -- S comes from exact 16-bit products accumulated in fp32, so L is
 accurate to a few fp32 ulps of the scores."""
 import numpy as np
+import torch
 import pytest
 
 import gpu_util as gu
@@ -75,3 +76,38 @@ def test_bf16_d128_growing_max():
     inp.bits["K"] = bits
     inp.K = si.bf16_bits_to_f32(bits)
     _check(inp, False, "growing max", l_tol=1e-3)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 32),
+                                     ("fp32", 16), ("fp32", 128)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 257, 600])
+def test_lse_alone(N, causal, dtype, d):
+    """fa_lse (L without O, for a backward whose forward did not keep L):
+    against the oracle's plain definition, and bitwise equal to the forward's
+    L on the same inputs -- the same sweep with V left out."""
+    gu.note(f"case lse {dtype} d={d} N={N} causal={causal}")
+    inp = si.draw_custom(2, 2, N, d, dtype, seed=600 + N + d)
+    q, k, v = (gu.upload(inp, n) for n in ("Q", "K", "V"))
+    L = fa.lse(q, k, inp.wl.scale, causal)
+    _, Lf = fa.forward(q, k, v, inp.wl.scale, causal)
+    assert torch.equal(L, Lf)
+    _, Lr = oracle.attn_fwd(inp.Q, inp.K, inp.V, inp.wl.scale, causal)
+    el = float(np.abs(gu.to_f64(L) - Lr).max())
+    gu.note(f"  L {el:.3e}")
+    # fp32: the score dot products and the running sum each add a few
+    # roundings, so L is good to a few ulps of its own magnitude
+    bar = 8 * 2.0**-23 * max(1.0, float(np.abs(Lr).max())) if dtype == "fp32" else 1e-4
+    assert el <= bar, f"L abs err {el:.3e} > {bar:.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_lse_alone_large_scores(causal):
+    """Peaky rows: the running maximum moves past the lazy threshold often."""
+    gu.note(f"case lse large scores causal={causal}")
+    inp = si.draw_custom(1, 2, 700, 128, "bf16", seed=508, q_mult=8.0)
+    q, k = gu.upload(inp, "Q"), gu.upload(inp, "K")
+    L = fa.lse(q, k, inp.wl.scale, causal)
+    _, Lr = oracle.attn_fwd(inp.Q, inp.K, inp.V, inp.wl.scale, causal)
+    el = float(np.abs(gu.to_f64(L) - Lr).max())
+    assert el <= 1e-3, f"L abs err {el:.3e}"
