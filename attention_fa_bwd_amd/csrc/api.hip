@@ -32,6 +32,10 @@ bool matrix_core(int dtype, int d) {
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
+// The softmax scale of the attention calls: finite and positive (the
+// matrix-core backward feeds -L / scale into its score products).
+bool scale_ok(float scale) { return scale > 0.f && scale <= 3.0e38f; }
+
 // Common checks; returns FA_OK when the call may proceed.
 int check(int dtype, int B, int H, int N, int d, std::initializer_list<const void*> ptrs) {
     if (!dtype_ok(dtype) || !dims_ok(B, H, N, d)) return FA_EINVAL;
@@ -55,6 +59,7 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V, void* O, 
                int B, int H, int N, int d, float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, O, L});
     if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     if (matrix_core(dtype, d))
@@ -68,6 +73,7 @@ int fa_lse(int dtype, const void* Q, const void* K, float* L, int B, int H, int 
            float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, L});
     if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     if (matrix_core(dtype, d))
@@ -90,6 +96,7 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
            int N, int d, float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum, dK, dV});
     if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     const hipStream_t st = (hipStream_t)stream;
@@ -110,6 +117,7 @@ int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const vo
                 float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dK, dV});
     if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
     if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
     return hip_status(fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d},
@@ -121,6 +129,7 @@ int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V, const void
               float scale, int causal, void* stream) {
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum});
     if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
     if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
     return hip_status(fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d},

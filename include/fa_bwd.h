@@ -24,7 +24,10 @@
  *              exceed the half range (|dS| > 65504) are outside the contract.
  *   Scores     S_ij = scale * Q_i . K_j; L_i = log sum_j exp(S_ij) over the
  *              visible keys (natural log).  causal != 0 hides key j from
- *              query i when j > i (0-based, diagonal kept).
+ *              query i when j > i (0-based, diagonal kept).  The softmax
+ *              scale (1/sqrt(d) on the pages) must be finite and positive:
+ *              the attention calls return FA_EINVAL otherwise (the
+ *              convert step only multiplies by it and takes any value).
  *   Pointers   device pointers (hipMalloc'd or equivalent), owned by the
  *              caller, at least 16-byte aligned.  Outputs must not alias
  *              inputs.  The library allocates nothing and keeps no mutable
@@ -37,7 +40,8 @@
  *              Supported head dims: d in {16, 32, 64, 128} for both dtypes.
  *   Errors     every call returns an fa_status_t.  Arguments are validated
  *              before any device work: FA_EINVAL for a NULL pointer, a
- *              non-positive or oversized dimension or an unknown dtype;
+ *              non-positive or oversized dimension, an unknown dtype or a
+ *              softmax scale that is not finite and positive;
  *              FA_EUNSUPPORTED for an unsupported head dim.  FA_EHIP when the
  *              HIP runtime reports an error (no device, launch failure); the
  *              raw hipError_t is available from fa_last_hip_error().  No call

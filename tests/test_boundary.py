@@ -65,6 +65,13 @@ def test_invalid_arguments_rejected_before_device_work():
     assert lib.fa_lse(1, p, p, None, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
     assert lib.fa_lse(2, p, p + 8, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL   # misaligned
     assert lib.fa_lse(5, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
+    # the softmax scale must be finite and positive for the attention calls
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        assert lib.fa_fwd_lse(1, p, p, p, p, p, 1, 1, 8, 128, bad, 0, None) == fa.FA_EINVAL
+        assert lib.fa_lse(1, p, p, p, 1, 1, 8, 64, bad, 1, None) == fa.FA_EINVAL
+        assert lib.fa_bwd(1, p, p, p, p, p, p, p, p, p, 1, 1, 8, 64, bad, 0, None) == fa.FA_EINVAL
+        assert lib.fa_bwd_dkdv(1, p, p, p, p, p, p, p, p, 1, 1, 8, 128, bad, 0, None) == fa.FA_EINVAL
+        assert lib.fa_bwd_dq(2, p, p, p, p, p, p, p, 1, 1, 8, 128, bad, 1, None) == fa.FA_EINVAL
     assert lib.fa_bwd_preprocess(1, p, p, p, None, 1, 1, 8, 64, None) == fa.FA_EINVAL
     assert lib.fa_bwd_convert_dq(0, None, p, 1, 1, 8, 64, 0.1, None) == fa.FA_EINVAL
 
