@@ -161,12 +161,14 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
         if (mf) {
-            // scores in exp2 units, masked where needed
+            // raw scores, masked where needed; the block maximum is taken on
+            // them and scaled once (the scale is positive, so the maximum of
+            // the scaled scores is the scaled maximum, exactly)
             float s2[32];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                s2[r] = S0[r] * sc;
-                s2[16 + r] = S1[r] * sc;
+                s2[r] = S0[r];
+                s2[16 + r] = S1[r];
             }
             if (j >= full) {
 #pragma unroll
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
             float m4[4] = {s2[0], s2[1], s2[2], s2[3]};
 #pragma unroll
             for (int e = 4; e < 32; ++e) m4[e & 3] = fmaxf(m4[e & 3], s2[e]);
-            float bm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+            float bm = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])) * sc;
             bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
             const bool rebase = bm > mu + kLazy;
             if (__ballot(rebase)) {
@@ -192,12 +194,13 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
-            // terms grouped by operation, the denominator summed in four
-            // interleaved partial sums, so that no result feeds the very next
-            // instruction
+            // terms grouped by operation (the scaling and the subtraction of
+            // the running maximum are one fused multiply-add), the
+            // denominator summed in four interleaved partial sums, so that no
+            // result feeds the very next instruction
             float p[32];
 #pragma unroll
-            for (int e = 0; e < 32; ++e) p[e] = s2[e] - mu;
+            for (int e = 0; e < 32; ++e) p[e] = __builtin_fmaf(s2[e], sc, -mu);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < 32; ++e) p[e] = __builtin_amdgcn_exp2f(p[e]);
