@@ -91,23 +91,6 @@ __device__ __forceinline__ v16x8_t bias_ones() {
     return as_v16x8(make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
 }
 
-// P and dS of accumulator elements r, r + 1 (one packed bf16 pair each).
-template <typename E, bool MASK>
-__device__ __forceinline__ void pds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
-                                         int key, int qrow, uint32_t& pp, uint32_t& pd) {
-    float p[2], d[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int e = r + u;
-        float x = S[e] * sc;
-        if (MASK && key > qrow + 8 * (e >> 2) + (e & 3)) x = -INFINITY;
-        p[u] = __builtin_amdgcn_exp2f(x);
-        d[u] = p[u] * dP[e];
-    }
-    pp = E::pack2(p[0], p[1]);
-    pd = E::pack2(d[0], d[1]);
-}
-
 // dS of elements r, r + 1 from P (already exponentiated, in S) and dP, and
 // both pairs packed.
 template <typename E>
@@ -143,10 +126,25 @@ __device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, i
             S = E::mma(lds_b128(sQ + off), kt[dk], S);
             dP = E::mma(lds_b128(sdO + off), vt[dk], dP);
         }
+        // P and dS, masked, grouped by operation eight elements at a time,
+        // so that dependent instructions stand eight apart
+        const int qrow = q0 + 32 * qb + 4 * h;
         uint32_t pk[8], dk[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            pds_pair<E, true>(S, dP, 2 * j, sc, key, q0 + 32 * qb + 4 * h, pk[j], dk[j]);
+        for (int g = 0; g < 2; ++g) {
+#pragma unroll
+            for (int e = 8 * g; e < 8 * g + 8; ++e) {
+                float x = S[e] * sc;
+                if (key > qrow + 8 * (e >> 2) + (e & 3)) x = -INFINITY;
+                S[e] = x;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 8 * g; e < 8 * g + 8; ++e) S[e] = __builtin_amdgcn_exp2f(S[e]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 4 * g; j < 4 * g + 4; ++j) ds_finish<E>(S, dP, 2 * j, pk[j], dk[j]);
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
             const int slab = ((2 * qb + hh) * 4 + s) * SLAB + l * 16;
