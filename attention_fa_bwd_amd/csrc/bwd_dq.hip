@@ -52,25 +52,6 @@ constexpr int OFF_DS = OFF_V + NVB * TILE;  // 2 buffers
 constexpr int LDS_BYTES = OFF_DS + 2 * DSB;
 static_assert(LDS_BYTES == 144 * 1024, "LDS plan");
 
-// dS of accumulator elements r, r + 1 as one packed bf16 pair.  MASK applies
-// key > query (causal) and key >= N element by element.
-template <typename E, bool MASK, bool CAUSAL>
-__device__ __forceinline__ uint32_t ds_pair(const f32x16_t& S, const f32x16_t& dP, int r, float sc,
-                                            float Lq, float Dq, int krow, int q, int N) {
-    float d[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int e = r + u;
-        float x = __builtin_fmaf(S[e], sc, -Lq);
-        if (MASK) {
-            const int key = krow + 8 * (e >> 2) + (e & 3);
-            if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
-        }
-        d[u] = __builtin_amdgcn_exp2f(x) * (dP[e] - Dq);
-    }
-    return E::pack2(d[0], d[1]);
-}
-
 // dS of elements r, r + 1 from P (already exponentiated, in S) and dP,
 // packed.
 template <typename E>
@@ -111,10 +92,26 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
                 S = E::mma(lds_b128(sK + off), qt[dk], S);
                 dP = E::mma(lds_b128(sV + off), gt[dk], dP);
             }
+            // dS, masked, grouped by operation eight elements at a time, so
+            // that dependent instructions stand eight apart
+            const int krow = k0 + 32 * mb + 4 * h;
             uint32_t pk[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                pk[j] = ds_pair<E, MASK, CAUSAL>(S, dP, 2 * j, sc, Lq, Dq, k0 + 32 * mb + 4 * h, q, N);
+            for (int g = 0; g < 2; ++g) {
+#pragma unroll
+                for (int e = 8 * g; e < 8 * g + 8; ++e) {
+                    float x = __builtin_fmaf(S[e], sc, -Lq);
+                    const int key = krow + 8 * (e >> 2) + (e & 3);
+                    if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
+                    S[e] = x;
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int e = 8 * g; e < 8 * g + 8; ++e) S[e] = __builtin_amdgcn_exp2f(S[e]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 4 * g; j < 4 * g + 4; ++j) pk[j] = ds_finish<E>(S, dP, 2 * j, Dq);
+            }
             store(mb, pk);
         }
         return;
