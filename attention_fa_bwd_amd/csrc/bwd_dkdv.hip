@@ -1,5 +1,5 @@
 // bwd_dkdv.hip -- key-outer pass of the FA2 backward on gfx950 matrix cores:
-// dK and dV for bf16, head dim 128.
+// dK and dV for bf16 and fp16, head dim 128.
 //
 // Method (FA2 chapter 16): one workgroup per (key block of 128 keys, head,
 // batch), key blocks outer and query tiles inner (sec 16.2); per query tile
@@ -17,7 +17,7 @@
 //   * score waves 0..3 own keys [32 s, 32 s + 32).  Their K^T and V^T B-operand
 //     fragments stay in registers; per tile they form S = Q K^T and
 //     dP = dO V^T (query on rows, key on lanes), P = exp2(S scale log2(e) -
-//     L log2(e)) and dS = P (dP - D), and store P and dS (bf16) to LDS in
+//     L log2(e)) and dS = P (dP - D), and store P and dS (16-bit) to LDS in
 //     their own register order, one 1 KiB slab per (16-query step, key group);
 //   * gradient waves 4..7 own one output each, dV^T (waves 4, 5) or dK^T
 //     (waves 6, 7), for rows [64 (g % 2), +64) of d and all 128 keys
@@ -44,7 +44,7 @@ constexpr int BC = 128;                  // keys per workgroup
 constexpr int BR = 64;                   // queries per tile
 constexpr int NWAVE = 8;
 constexpr int TILE = BR * ROWB;          // 16 KiB
-constexpr int SLAB = 1024;               // one 16-query x 32-key bf16 operand, lane order
+constexpr int SLAB = 1024;               // one 16-query x 32-key 16-bit operand, lane order
 constexpr int PDS = 4 * 4 * SLAB;        // P (or dS) of one tile: 16 KiB
 constexpr int OFF_Q = 0;                 // 3 buffers
 constexpr int OFF_DO = 3 * TILE;         // 3 buffers

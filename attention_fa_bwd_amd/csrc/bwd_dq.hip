@@ -1,5 +1,5 @@
 // bwd_dq.hip -- query-outer pass of the FA2 backward on gfx950 matrix cores:
-// dQ (unscaled, fp32) for bf16, head dim 128.
+// dQ (unscaled, fp32) for bf16 and fp16, head dim 128.
 //
 // FA2 chapter 16 sec 16.3 weighs adding dQ partials with global atomics
 // against a second pass.  On MI355X the fp32 atomics run at about 340 G/s
@@ -16,7 +16,7 @@
 //   * score waves 0..3 own queries [32 s, 32 s + 32) of the block; their Q^T
 //     and dO^T B-operand fragments, L and D stay in registers.  Per key block
 //     of 64 they form S^T = K Q^T and dP^T = V dO^T (key on rows, query on
-//     lanes) and dS = P (dP - D), and store dS (bf16) to LDS in their own
+//     lanes) and dS = P (dP - D), and store dS (16-bit) to LDS in their own
 //     register order, one 1 KiB slab per (16-key step, query group);
 //   * gradient waves 4..7 own columns [32 g, 32 g + 32) of d of dQ for all
 //     128 queries (accumulators in registers).  One key block behind, they
@@ -42,7 +42,7 @@ constexpr int BQ = 128;                  // queries per workgroup
 constexpr int BK = 64;                   // keys per block
 constexpr int NWAVE = 8;
 constexpr int TILE = BK * ROWB;          // 16 KiB
-constexpr int SLAB = 1024;               // one 32-query x 16-key bf16 operand, lane order
+constexpr int SLAB = 1024;               // one 32-query x 16-key 16-bit operand, lane order
 constexpr int DSB = 4 * 4 * SLAB;        // dS of one block: 16 KiB
 constexpr int NKB = 4;                   // K buffers: blocks p - 1 .. p + 2
 constexpr int NVB = 3;                   // V buffers: blocks p .. p + 2

@@ -1,4 +1,4 @@
-// fwd_mfma.hip -- attention forward on gfx950 matrix cores, bf16, head dim 128:
+// fwd_mfma.hip -- attention forward on gfx950 matrix cores, bf16 and fp16, head dim 128:
 // O and the logsumexp L (supporting step: they feed the backward).
 //
 // Query blocks outer, key blocks inner, online softmax per query
