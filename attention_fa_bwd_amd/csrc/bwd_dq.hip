@@ -27,8 +27,9 @@
 //     ds_read_b64_tr_b16 -- each fragment feeds eight products, one per query
 //     group -- and dS straight from the slabs;
 //   * K blocks rotate through four LDS buffers (score waves read block p,
-//     gradient waves block p - 1, block p + 1 has landed, direct-to-LDS
-//     copies fill block p + 2, spread over the gradient steps), V blocks
+//     gradient waves block p - 1, the copies of block p + 1, issued one
+//     phase earlier, complete before the phase's barrier, and direct-to-LDS
+//     copies of block p + 2 go out spread over the gradient steps), V blocks
 //     through three, dS through two (88 KiB).  One barrier per block;
 //   * rows at or beyond N are staged as copies of row N - 1; in the last key
 //     block their P is forced to 0, and query rows at or beyond N are not
