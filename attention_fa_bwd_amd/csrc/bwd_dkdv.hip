@@ -195,11 +195,44 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
         dP0 = E::mma(ag[i % 3], vt[i], dP0);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // Block 0's P and dS under block 1's products, software-pipelined so that
-    // no result is used by the very next instruction: after the first pair
-    // of products all sixteen scores go to exp2 units; step k then takes the
-    // exponentials of pair k and finishes (dS, packing) pair k - 1.
+    // Block 0's P and dS under block 1's products.  A wave's next product
+    // waits for the matrix pipe, and its vector work behind that product
+    // waits too, so the arithmetic sits between products, each piece pinned
+    // to its place: after product m (m = 0..15) come the exponential of
+    // element m, the scaling of element m + 2, dS = P dP of element m - 2 and,
+    // every other product, the packing of one pair -- 18 to 28 cycles under
+    // each 32-cycle product, no result used by the next instruction.
     uint32_t pk[8], dk[8];
+    auto scl = [&](int e) {
+        float t = S0[e] * sc;
+        pin(t);
+        S0[e] = t;
+    };
+    auto ex = [&](int e) {
+        float t = __builtin_amdgcn_exp2f(S0[e]);
+        pin(t);
+        S0[e] = t;
+    };
+    auto dsm = [&](int e) {
+        float t = S0[e] * dP0[e];
+        pin(t);
+        dP0[e] = t;
+    };
+    auto pack = [&](int j) {
+        uint32_t a = E::pack2(S0[2 * j], S0[2 * j + 1]), b = E::pack2(dP0[2 * j], dP0[2 * j + 1]);
+        pin(a);
+        pin(b);
+        pk[j] = a;
+        dk[j] = b;
+    };
+    auto arith = [&](int m) {
+        ex(m);
+        if (m + 2 < 16) scl(m + 2);
+        if (m >= 2) dsm(m - 2);
+        if (m >= 4 && !(m & 1)) pack((m - 4) >> 1);
+    };
+    scl(0);
+    scl(1);
 #pragma unroll
     for (int i = 8; i < 16; ++i) {
         const int k = i - 8;
@@ -208,16 +241,18 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
             ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
         }
         S1 = E::mma(aq[i % 3], kt[i - 8], S1);
+        __builtin_amdgcn_sched_barrier(0);
+        arith(2 * k);
+        __builtin_amdgcn_sched_barrier(0);
         dP1 = E::mma(ag[i % 3], vt[i - 8], dP1);
-        if (k == 0)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) S0[e] *= sc;
-        S0[2 * k] = __builtin_amdgcn_exp2f(S0[2 * k]);
-        S0[2 * k + 1] = __builtin_amdgcn_exp2f(S0[2 * k + 1]);
-        if (k >= 1) ds_finish<E>(S0, dP0, 2 * k - 2, pk[k - 1], dk[k - 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        arith(2 * k + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    ds_finish<E>(S0, dP0, 14, pk[7], dk[7]);
+    dsm(14);
+    pack(6);
+    dsm(15);
+    pack(7);
     // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {

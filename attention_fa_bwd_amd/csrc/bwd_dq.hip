@@ -133,35 +133,55 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
         S1 = E::mma(op[i % 3], qt[1][i], S1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // Exponentials of S under the dP products, four elements a step: step j
-    // exponentiates chunk j (scaled one step earlier) and scales chunk j + 1.
-    auto scale4 = [&](int c) {
+    // Exponentials of S under the dP products.  A wave's next product waits
+    // for the matrix pipe, and its vector work behind that product waits too,
+    // so the arithmetic sits between the two products of a step (about 27
+    // cycles of it under each 32-cycle product): half-step k exponentiates
+    // elements 2k, 2k + 1 of the 32 (scaled one step earlier) and scales
+    // elements 2k + 4, 2k + 5.  Elements 0..15 are S0's, 16..31 S1's.
+    auto scale2 = [&](int k) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (c < 4)
-                S0[4 * c + e] = __builtin_fmaf(S0[4 * c + e], sc, -Lq[0]);
-            else
-                S1[4 * (c - 4) + e] = __builtin_fmaf(S1[4 * (c - 4) + e], sc, -Lq[1]);
+        for (int e = 2 * k; e < 2 * k + 2; ++e) {
+            if (e < 16) {
+                float t = __builtin_fmaf(S0[e], sc, -Lq[0]);
+                pin(t);
+                S0[e] = t;
+            } else {
+                float t = __builtin_fmaf(S1[e - 16], sc, -Lq[1]);
+                pin(t);
+                S1[e - 16] = t;
+            }
         }
     };
-    auto exp4 = [&](int c) {
+    auto exp2 = [&](int k) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (c < 4)
-                S0[4 * c + e] = __builtin_amdgcn_exp2f(S0[4 * c + e]);
-            else
-                S1[4 * (c - 4) + e] = __builtin_amdgcn_exp2f(S1[4 * (c - 4) + e]);
+        for (int e = 2 * k; e < 2 * k + 2; ++e) {
+            if (e < 16) {
+                float t = __builtin_amdgcn_exp2f(S0[e]);
+                pin(t);
+                S0[e] = t;
+            } else {
+                float t = __builtin_amdgcn_exp2f(S1[e - 16]);
+                pin(t);
+                S1[e - 16] = t;
+            }
         }
     };
-    scale4(0);
+    scale2(0);
+    scale2(1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int u = 8 + j;
         if (u + 2 < 16) op[(u + 2) % 3] = lds_b128(sV + so[j + 2]);
         dP0 = E::mma(op[u % 3], gt[0][j], dP0);
+        __builtin_amdgcn_sched_barrier(0);
+        exp2(2 * j);
+        if (2 * j + 2 < 16) scale2(2 * j + 2);
+        __builtin_amdgcn_sched_barrier(0);
         dP1 = E::mma(op[u % 3], gt[1][j], dP1);
-        exp4(j);
-        if (j + 1 < 8) scale4(j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        exp2(2 * j + 1);
+        if (2 * j + 3 < 16) scale2(2 * j + 3);
         __builtin_amdgcn_sched_barrier(0);
     }
     finish(S0, dP0, Dq[0], 0);

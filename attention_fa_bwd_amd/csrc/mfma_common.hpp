@@ -202,6 +202,15 @@ struct TileCopier {
     }
 };
 
+// Pins the computation of v to this point of the instruction stream: an empty
+// volatile statement that takes v in a register and gives it back.  The
+// statement keeps its place among other side-effecting operations (LDS
+// accesses, sched_barrier), so the arithmetic that produces v cannot drift
+// past it.  sched_barrier alone only constrains the final machine scheduler,
+// which sees pure arithmetic where instruction selection has already put it.
+__device__ __forceinline__ void pin(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 // LDS byte address of a pointer into a __shared__ array (wave-uniform).
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)__builtin_amdgcn_readfirstlane(
