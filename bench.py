@@ -199,6 +199,39 @@ def lse_time(wl, causal: bool, inputs, reps: int = 5):
     return a.elapsed_time(b) / reps
 
 
+def fwd_bwd_time(wl, causal: bool, inputs, reps: int = 5):
+    """Time of a whole training step of the attention (not the metric's
+    step): fa_fwd_lse, then the backward (preprocess, both passes, convert),
+    all on the launch stream; HIP events around `reps` steps after a warm-up."""
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    q, k, v, do = inputs
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    L = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    D = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dqa = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        fa.fa_fwd_lse(q, k, v, o, L, wl.scale, causal, stream)
+        fa.fa_bwd_preprocess(o, do, D, dqa, stream)
+        fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, wl.scale, causal, stream)
+        fa.fa_bwd_convert_dq(dqa, dq, wl.scale, stream)
+
+    one()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        one()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def cpu_baseline(wl, causal: bool, budget_s: float):
     """The oracle's full backward (by definition) on a bounded sample of heads."""
     import numpy as np
@@ -274,6 +307,10 @@ def main():
         lfl = 0.2 * flops  # S only: 2·B·H·N²·d (×½ causal)
         r["recompute_L"] = {"ms": round(lms, 4), "tflops": round(lfl / (lms * 1e-3) / 1e12, 3),
                             "step_ms_with_it": round(r["ms_per_step"] + lms, 4)}
+        tms = fwd_bwd_time(wl, causal, (up["Q"], up["K"], up["V"], up["dO"]))
+        tfl = 1.4 * flops  # forward 4 + backward 10: 14·B·H·N²·d (×½ causal)
+        r["forward_backward"] = {"ms": round(tms, 4),
+                                 "tflops": round(tfl / (tms * 1e-3) / 1e12, 3)}
         results[causal] = r
         del o, L
     prim = results[args.causal]
@@ -307,6 +344,7 @@ def main():
         "kernels": prim["kernels"],
         "forward": prim["forward"],
         "recompute_L": prim["recompute_L"],
+        "forward_backward": prim["forward_backward"],
     }
     if len(results) > 1:
         other = results[not args.causal]
@@ -316,7 +354,7 @@ def main():
             "pct_bf16_peak": round(other["pct_peak"], 2),
             "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
             "kernels": other["kernels"], "forward": other["forward"],
-            "recompute_L": other["recompute_L"]}
+            "recompute_L": other["recompute_L"], "forward_backward": other["forward_backward"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
     else:
