@@ -14,11 +14,13 @@
 // gfx950 mapping: 8 waves, two per SIMD, in two roles that overlap on each
 // SIMD (one wave's matrix-core work runs while the other computes or waits on
 // LDS):
-//   * score waves 0..3 own keys [32 s, 32 s + 32).  Their K^T and V^T B-operand
-//     fragments stay in registers; per tile they form S = Q K^T and
+//   * score wave s owns key groups 2 (s % 2) and 2 (s % 2) + 1 (64 keys; K^T
+//     and V^T B-operand fragments in registers) for query rows
+//     [32 (s / 2), +32) of every tile, so that each Q or dO fragment read
+//     from LDS feeds two products; per tile it forms S = Q K^T and
 //     dP = dO V^T (query on rows, key on lanes), P = exp2(S scale log2(e) -
-//     L log2(e)) and dS = P (dP - D), and store P and dS (16-bit) to LDS in
-//     their own register order, one 1 KiB slab per (16-query step, key group);
+//     L log2(e)) and dS = P (dP - D), and stores P and dS (16-bit) to LDS in
+//     its own register order, one 1 KiB slab per (16-query step, key group);
 //   * gradient waves 4..7 own one output each, dV^T (waves 4, 5) or dK^T
 //     (waves 6, 7), for rows [64 (g % 2), +64) of d and all 128 keys
 //     (accumulators in registers).  One tile behind the score waves, they
@@ -100,181 +102,104 @@ __device__ __forceinline__ void ds_finish(const f32x16_t& P, const f32x16_t& dP,
     pd = E::pack2(P[r] * dP[r], P[r + 1] * dP[r + 1]);
 }
 
-// Score role on a diagonal tile (causal mask applied element by element):
-// block by block, no interleaving -- two such tiles per workgroup, and the
-// mask needs registers the interleaved order does not have to spare.
-template <typename E, bool RAGGED>
-__device__ __forceinline__ void score_step_diag(unsigned char* smem, int qbuf, int pbuf, int q0,
-                                                int N, int key, float sc, float fac,
-                                                const float (&st)[2], const v16x8_t (&kt)[8],
-                                                const v16x8_t (&vt)[8], int s, int l) {
-    const int h = l >> 5, n = l & 31;
-    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
-    const unsigned char* sdO = smem + OFF_DO + qbuf * TILE;
-    unsigned char* sP = smem + OFF_P + pbuf * PDS;
-    unsigned char* sS = smem + OFF_DS + pbuf * PDS;
-    const v16x8_t ones = bias_ones();
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        v16x8_t bS, bD;
-        bias_operands<RAGGED>(st[qb], q0 + 32 * qb + n, N, h, fac, bS, bD);
-        f32x16_t S = mfma(bS, ones, f32x16_t{}), dP = mfma(bD, ones, f32x16_t{});
-        const int row = 32 * qb + n;
-#pragma unroll
-        for (int dk = 0; dk < 8; ++dk) {
-            const int off = tile_off(row, 32 * dk + 16 * h);
-            S = E::mma(lds_b128(sQ + off), kt[dk], S);
-            dP = E::mma(lds_b128(sdO + off), vt[dk], dP);
-        }
-        // P and dS, masked, grouped by operation eight elements at a time,
-        // so that dependent instructions stand eight apart
-        const int qrow = q0 + 32 * qb + 4 * h;
-        uint32_t pk[8], dk[8];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-#pragma unroll
-            for (int e = 8 * g; e < 8 * g + 8; ++e) {
-                float x = S[e] * sc;
-                if (key > qrow + 8 * (e >> 2) + (e & 3)) x = -INFINITY;
-                S[e] = x;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int e = 8 * g; e < 8 * g + 8; ++e) S[e] = __builtin_amdgcn_exp2f(S[e]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 4 * g; j < 4 * g + 4; ++j) ds_finish<E>(S, dP, 2 * j, pk[j], dk[j]);
-        }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int slab = ((2 * qb + hh) * 4 + s) * SLAB + l * 16;
-            *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
-            *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
-        }
-    }
-}
-
-// Score role: S, dP, P, dS of query tile q0 (below the causal diagonal, or
-// any tile without the mask) for this wave's 32 keys.  RAGGED: the tile runs
-// past row N.  Issue order (pinned with sched_barrier): operand reads run two
-// MFMA pairs ahead; the S/dP products of block 1 are interleaved with the P/dS
-// arithmetic of block 0; block 1's arithmetic then overlaps the gradient wave
-// sharing the SIMD.
-template <typename E, bool RAGGED>
+// Score role, wave w: key groups 2 kp and 2 kp + 1 (kp = w % 2; 64 keys, K^T
+// and V^T fragments in registers) for query rows [32 qh, 32 qh + 32) of the
+// tile (qh = w / 2), so that every Q or dO fragment read from LDS feeds two
+// products.  S and dP of both key groups start from the row statistics
+// (bias products), P = exp2(S scale log2 e), dS = P dP; P and dS go to the
+// slabs (16-query step t = 2 qh + hh, key group 2 kp + c), lane-ordered.
+// RAGGED: the tile runs past row N.  DIAG: the tile crosses the causal
+// diagonal and the mask is applied element by element.  Operand reads run
+// two products ahead, and the exponentials sit between the dP products,
+// each pinned to its place.
+template <typename E, bool RAGGED, bool DIAG>
 __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pbuf, int q0, int N,
-                                           float sc, float fac, const float (&st)[2],
-                                           const v16x8_t (&kt)[8], const v16x8_t (&vt)[8],
-                                           const int (&so)[8], int s, int l) {
+                                           int k0, float sc, float fac, float st,
+                                           const v16x8_t (&kt)[2][8], const v16x8_t (&vt)[2][8],
+                                           const int (&so)[8], int kp, int qh, int l) {
     const int h = l >> 5, n = l & 31;
-    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE;
+    // rows 32 qh + n share row n's swizzle
+    const unsigned char* sQ = smem + OFF_Q + qbuf * TILE + 32 * ROWB * qh;
     const unsigned char* sdO = sQ + (OFF_DO - OFF_Q);
     unsigned char* sP = smem + OFF_P + pbuf * PDS;
     unsigned char* sS = smem + OFF_DS + pbuf * PDS;
     const v16x8_t ones = bias_ones();
-
-    // operand of step i (i = 0..15: block i / 8, d-chunk i % 8); rows 32 + n
-    // share row n's swizzle
-    auto opoff = [&](int i) { return so[i & 7] + 32 * ROWB * (i >> 3); };
-    v16x8_t aq[3], ag[3];
-    aq[0] = lds_b128(sQ + opoff(0));
-    ag[0] = lds_b128(sdO + opoff(0));
-    aq[1] = lds_b128(sQ + opoff(1));
-    ag[1] = lds_b128(sdO + opoff(1));
-
     v16x8_t bS, bD;
-    bias_operands<RAGGED>(st[0], q0 + n, N, h, fac, bS, bD);
-    f32x16_t S0 = mfma(bS, ones, f32x16_t{}), dP0 = mfma(bD, ones, f32x16_t{});
-    bias_operands<RAGGED>(st[1], q0 + 32 + n, N, h, fac, bS, bD);
-    f32x16_t S1 = mfma(bS, ones, f32x16_t{}), dP1 = mfma(bD, ones, f32x16_t{});
+    bias_operands<RAGGED>(st, q0 + 32 * qh + n, N, h, fac, bS, bD);
+    const f32x16_t zS = mfma(bS, ones, f32x16_t{});
     __builtin_amdgcn_sched_barrier(0);
+
+    v16x8_t aq[3], ag[3];
+    aq[0] = lds_b128(sQ + so[0]);
+    aq[1] = lds_b128(sQ + so[1]);
+    f32x16_t S0 = zS, S1 = zS;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
-        ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
-        S0 = E::mma(aq[i % 3], kt[i], S0);
-        dP0 = E::mma(ag[i % 3], vt[i], dP0);
+        if (i + 2 < 8) aq[(i + 2) % 3] = lds_b128(sQ + so[i + 2]);
+        else ag[i - 6] = lds_b128(sdO + so[i - 6]);
+        S0 = E::mma(aq[i % 3], kt[0][i], S0);
+        S1 = E::mma(aq[i % 3], kt[1][i], S1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // Block 0's P and dS under block 1's products.  A wave's next product
-    // waits for the matrix pipe, and its vector work behind that product
-    // waits too, so the arithmetic sits between products, each piece pinned
-    // to its place: after product m (m = 0..15) come the exponential of
-    // element m, the scaling of element m + 2, dS = P dP of element m - 2 and,
-    // every other product, the packing of one pair -- 18 to 28 cycles under
-    // each 32-cycle product, no result used by the next instruction.
-    uint32_t pk[8], dk[8];
+    // elements e = 0..31: S0's, then S1's.  DIAG: elements above the
+    // diagonal (key past the query) get -inf, so P = 0 there.
+    // element e: key key0 + 32 (e / 16), row qrow + 8 ((e % 16) / 4) + e % 4;
+    // masked when (key0 - qrow) exceeds a constant of e
+    const int kmq = (k0 + 64 * kp + n) - (q0 + 32 * qh + 4 * h);
     auto scl = [&](int e) {
-        float t = S0[e] * sc;
+        f32x16_t& S = e < 16 ? S0 : S1;
+        float t = S[e & 15] * sc;
+        if (DIAG && kmq > 8 * ((e & 15) >> 2) + (e & 3) - 32 * (e >> 4)) t = -INFINITY;
         pin(t);
-        S0[e] = t;
+        S[e & 15] = t;
     };
     auto ex = [&](int e) {
-        float t = __builtin_amdgcn_exp2f(S0[e]);
+        f32x16_t& S = e < 16 ? S0 : S1;
+        float t = __builtin_amdgcn_exp2f(S[e & 15]);
         pin(t);
-        S0[e] = t;
+        S[e & 15] = t;
     };
-    auto dsm = [&](int e) {
-        float t = S0[e] * dP0[e];
-        pin(t);
-        dP0[e] = t;
-    };
-    auto pack = [&](int j) {
-        uint32_t a = E::pack2(S0[2 * j], S0[2 * j + 1]), b = E::pack2(dP0[2 * j], dP0[2 * j + 1]);
-        pin(a);
-        pin(b);
-        pk[j] = a;
-        dk[j] = b;
-    };
-    auto arith = [&](int m) {
-        ex(m);
-        if (m + 2 < 16) scl(m + 2);
-        if (m >= 2) dsm(m - 2);
-        if (m >= 4 && !(m & 1)) pack((m - 4) >> 1);
-    };
+    // dP (its bias product only now, so that its accumulator is not live
+    // through the S products); after product m (m = 0..15) the exponentials
+    // of elements 2m, 2m + 1, scaled (and masked) one product earlier
+    const f32x16_t zD = mfma(bD, ones, f32x16_t{});
+    f32x16_t dP0 = zD, dP1 = zD;
     scl(0);
     scl(1);
 #pragma unroll
-    for (int i = 8; i < 16; ++i) {
-        const int k = i - 8;
-        if (i + 2 < 16) {
-            aq[(i + 2) % 3] = lds_b128(sQ + opoff(i + 2));
-            ag[(i + 2) % 3] = lds_b128(sdO + opoff(i + 2));
+    for (int i = 0; i < 8; ++i) {
+        if (i + 2 < 8) ag[(i + 2) % 3] = lds_b128(sdO + so[i + 2]);
+        dP0 = E::mma(ag[i % 3], vt[0][i], dP0);
+        __builtin_amdgcn_sched_barrier(0);
+        ex(4 * i);
+        ex(4 * i + 1);
+        scl(4 * i + 2);
+        scl(4 * i + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        dP1 = E::mma(ag[i % 3], vt[1][i], dP1);
+        __builtin_amdgcn_sched_barrier(0);
+        ex(4 * i + 2);
+        ex(4 * i + 3);
+        if (i + 1 < 8) {
+            scl(4 * i + 4);
+            scl(4 * i + 5);
         }
-        S1 = E::mma(aq[i % 3], kt[i - 8], S1);
-        __builtin_amdgcn_sched_barrier(0);
-        arith(2 * k);
-        __builtin_amdgcn_sched_barrier(0);
-        dP1 = E::mma(ag[i % 3], vt[i - 8], dP1);
-        __builtin_amdgcn_sched_barrier(0);
-        arith(2 * k + 1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    dsm(14);
-    pack(6);
-    dsm(15);
-    pack(7);
-    // slab (t = 2 qb + hh, key group s), lane-ordered 16 bytes
+    // dS = P dP and the packing, grouped by operation, then the slabs
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int slab = (hh * 4 + s) * SLAB + l * 16;
-        *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
-        *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
-    }
-    // block 1's P and dS with nothing else to overlap: grouped by operation
-    // so that dependent instructions stand sixteen apart
+    for (int c = 0; c < 2; ++c) {
+        const f32x16_t& P = c ? S1 : S0;
+        const f32x16_t& dP = c ? dP1 : dP0;
+        uint32_t pk[8], dk[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) S1[e] *= sc;
-    __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 8; ++j) ds_finish<E>(P, dP, 2 * j, pk[j], dk[j]);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) S1[e] = __builtin_amdgcn_exp2f(S1[e]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ds_finish<E>(S1, dP1, 2 * j, pk[j], dk[j]);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const int slab = ((2 + hh) * 4 + s) * SLAB + l * 16;
-        *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
-        *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
+        for (int hh = 0; hh < 2; ++hh) {
+            const int slab = ((2 * qh + hh) * 4 + 2 * kp + c) * SLAB + l * 16;
+            *reinterpret_cast<uint4*>(sP + slab) = make_uint4(pk[4 * hh], pk[4 * hh + 1], pk[4 * hh + 2], pk[4 * hh + 3]);
+            *reinterpret_cast<uint4*>(sS + slab) = make_uint4(dk[4 * hh], dk[4 * hh + 1], dk[4 * hh + 2], dk[4 * hh + 3]);
+        }
     }
 }
 
@@ -337,7 +262,6 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
     const bool score = wave < 4;
     const int r4 = wave & 3;  // key group (score) or d block (gradient)
-    const int key = k0 + 32 * r4 + n;
 
     const int q_begin = CAUSAL ? k0 : 0;
     const int ntiles = (N - q_begin + BR - 1) / BR;
@@ -355,58 +279,51 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     // tile p - 1.  Each role has its own loop so that its registers never
     // coexist with the other role's.
     if (score) {
-        const int keyc = key < N ? key : N - 1;  // clamped: finite data, outputs not stored
-        v16x8_t kt[8], vt[8];
+        const int kp = r4 & 1, qh = r4 >> 1;  // key pair, query half of each tile
+        v16x8_t kt[2][8], vt[2][8];
 #pragma unroll
-        for (int dk = 0; dk < 8; ++dk) {
-            kt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
-            vt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
-        }
-        // row statistics of tile p in st, of tile p + 1 fetched during step p
-        const float* stat = h ? Dh : Lh;
-        const float* statn = stat + n;
-        const float fac = h ? -1.f : -1.f / scale;
-        // rows qn + n and qn + 32 + n, clamped into [0, N)
-        auto fetch2 = [&](int qn, float (&o)[2]) {
-            if (qn + BR <= N) {
-                o[0] = statn[qn];
-                o[1] = statn[qn + 32];
-            } else {
-                o[0] = fetch_stat(stat, qn + n, N);
-                o[1] = fetch_stat(stat, qn + 32 + n, N);
+        for (int c = 0; c < 2; ++c) {
+            const int kk = k0 + 64 * kp + 32 * c + n;
+            const int keyc = kk < N ? kk : N - 1;  // clamped: finite data, outputs not stored
+#pragma unroll
+            for (int dk = 0; dk < 8; ++dk) {
+                kt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * D + 16 * dk + 8 * h));
+                vt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * D + 16 * dk + 8 * h));
             }
-        };
+        }
+        // row statistic of this wave's rows in tile p in st (L on lane half
+        // 0, D on half 1), that of tile p + 1 fetched during step p
+        const float* stat = (h ? Dh : Lh) + 32 * qh;
+        const float fac = h ? -1.f : -1.f / scale;
+        auto fetch1 = [&](int qn) { return fetch_stat(stat, qn + n, N - 32 * qh); };
         int so[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
-        float st[2], nx[2];
-        fetch2(q_begin, st);
-        // diagonal tiles (causal only) in a loop of their own, then the rest;
-        // the waits before each barrier cover only LDS traffic, so the next
-        // tile's statistics stay in flight across it
+        float st = fetch1(q_begin);
+        // diagonal tiles (causal only) first, then the rest; the waits before
+        // each barrier cover only LDS traffic, so the next tile's statistic
+        // stays in flight across it
         int p = 0;
         for (; p < min(nmask, ntiles); ++p) {
             const int q0 = q_begin + p * BR;
-            fetch2(q0 + BR, nx);
+            const float nx = fetch1(q0 + BR);
             if (q0 + BR > N)
-                score_step_diag<E, true>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
+                score_step<E, true, true>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
             else
-                score_step_diag<E, false>(smem, p % 3, p & 1, q0, N, key, sc, fac, st, kt, vt, r4, l);
-            st[0] = nx[0];
-            st[1] = nx[1];
+                score_step<E, false, true>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
+            st = nx;
             __builtin_amdgcn_s_waitcnt(kLgkmOnly);
             __syncthreads();
         }
         for (; p <= ntiles; ++p) {
             if (p < ntiles) {
                 const int q0 = q_begin + p * BR;
-                fetch2(q0 + BR, nx);
+                const float nx = fetch1(q0 + BR);
                 if (q0 + BR > N)
-                    score_step<E, true>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
+                    score_step<E, true, false>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
                 else
-                    score_step<E, false>(smem, p % 3, p & 1, q0, N, sc, fac, st, kt, vt, so, r4, l);
-                st[0] = nx[0];
-                st[1] = nx[1];
+                    score_step<E, false, false>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
+                st = nx;
             }
             __builtin_amdgcn_s_waitcnt(kLgkmOnly);
             __syncthreads();
