@@ -2,7 +2,9 @@
 //
 // preprocess: D_i = sum_k O_ik dO_ik in fp32 (FA2 chapter 16, sec 16.1: the
 //   identity D_i = dO_i . O_i; sec 16.8 item 1: computed once before the main
-//   loop) and dq_accum := 0.
+//   loop) and dq_accum := 0 where the main step accumulates into it (the
+//   vector-ALU path); the matrix-core dQ pass (16-bit elements, d = 128)
+//   writes every dq_accum row itself, so there the zeroing is skipped.
 // convert:    dQ = scale * dq_accum, cast to the element type (sec 16.3: the
 //   separate kernel that applies the softmax scale to the fp32 buffer).
 //
@@ -13,7 +15,7 @@
 
 namespace fa {
 
-template <typename T, int D>
+template <typename T, int D, bool ZERO>
 __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ O,
                                                          const T* __restrict__ dO,
                                                          float* __restrict__ Dout,
@@ -38,9 +40,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ O
 #pragma unroll
         for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
         if (sub == 0) Dout[row] = acc;
-        float4* z = reinterpret_cast<float4*>(dqa + off);
+        if (ZERO) {
+            float4* z = reinterpret_cast<float4*>(dqa + off);
 #pragma unroll
-        for (int i = 0; i < VEC / 4; ++i) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int i = 0; i < VEC / 4; ++i) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
     }
 }
 
@@ -80,8 +84,10 @@ template <typename T, int D>
 static hipError_t pre_t(const void* O, const void* dO, float* Dv, float* dqa, Shape s,
                         hipStream_t st) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
-    hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3(grid_for(s.rows(), RPB)), dim3(256), 0,
-                       st, (const T*)O, (const T*)dO, Dv, dqa, s.rows());
+    // zeroing only where the main step accumulates (not 16-bit with d = 128)
+    constexpr bool ZERO = !(sizeof(T) == 2 && D == 128);
+    hipLaunchKernelGGL((preprocess_kernel<T, D, ZERO>), dim3(grid_for(s.rows(), RPB)), dim3(256),
+                       0, st, (const T*)O, (const T*)dO, Dv, dqa, s.rows());
     return hipGetLastError();
 }
 

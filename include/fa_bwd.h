@@ -98,10 +98,12 @@ int fa_lse(int dtype, const void* Q, const void* K, float* L,
 /*
  * fa_bwd_preprocess -- D_i = sum_k O_ik dO_ik with fp32 accumulation (FA2
  * chapter 16 sec 16.1, the identity D_i = dO_i . O_i, and sec 16.8 item 1:
- * computed once before the main loop), and dq_accum := 0 so that the main
- * kernel can accumulate into it.
+ * computed once before the main loop), and dq_accum := 0 for the dtype /
+ * head-dim pairs whose main step accumulates into it.
  *   in : O, dO [B,H,N,d] dtype
- *   out: D [B,H,N] fp32 (written), dq_accum [B,H,N,d] fp32 (zeroed)
+ *   out: D [B,H,N] fp32 (written); dq_accum [B,H,N,d] fp32: zeroed, except
+ *        for bf16 / fp16 with d = 128, where it is left untouched because
+ *        the dQ pass (fa_bwd, fa_bwd_dq) writes every element
  */
 int fa_bwd_preprocess(int dtype, const void* O, const void* dO,
                       float* D, float* dq_accum,
