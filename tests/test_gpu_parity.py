@@ -127,6 +127,29 @@ def test_edge_shapes(N, d, dtype, causal):
         _assert_grads(errs, gu.TOL[dtype], f"N={N} d={d} {dtype}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N", [300, 520])
+def test_multi_block_ragged_d128(N, dtype, causal):
+    """Head dim 128, 16-bit: more than one 256-query block of the dQ pass and
+    more than one 128-key block of the dK/dV pass, the last of each ragged
+    (N = 300: 44 rows in the second query block, so three of its four score
+    waves own only rows past N; N = 520: 8 rows in the third).  Full tensors
+    against the oracle, end to end and with the oracle's O and L."""
+    gu.note(f"case multi-block ragged N={N} d=128 {dtype} causal={causal}")
+    inp = si.draw_custom(2, 2, N, 128, dtype, seed=900 + N)
+    out = gu.run_gpu(inp, causal)
+    errs = gu.compare_full(inp, causal, out)
+    _assert_grads(errs, gu.TOL[dtype], f"N={N} {dtype} end to end")
+    O, L = oracle.attn_fwd(inp.Q, inp.K, inp.V, inp.wl.scale, causal)
+    Os = _stored(O, dtype)
+    out = gu.run_gpu(inp, causal, O=Os, L=L)
+    rq, rk, rv = oracle.flash_bwd_tiled(inp.Q, inp.K, inp.V, Os, inp.dO, L, inp.wl.scale, causal, 16, 12)
+    errs = {n: gu.rel_err(gu.to_f64(out[n]), r) for n, r in (("dq", rq), ("dk", rk), ("dv", rv))}
+    _assert_grads(errs, gu.TOL[dtype], f"N={N} {dtype} isolated")
+    assert not gu.invariants(inp, causal, out)["nan"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("q_mult", [4.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
