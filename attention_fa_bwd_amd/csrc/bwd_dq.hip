@@ -21,11 +21,13 @@
 //     while the dP products issue, then dS = P (dP - D), and store dS (16-bit)
 //     to LDS in their own register order, one 1 KiB slab per (16-key step,
 //     query group);
-//   * gradient waves 4..7 own columns [32 g, 32 g + 32) of d of dQ for all
-//     256 queries (accumulators in registers).  One key block behind, they
-//     read the K operand of that block (key on the contraction index) with
-//     ds_read_b64_tr_b16 -- each fragment feeds eight products, one per query
-//     group -- and dS straight from the slabs;
+//   * gradient wave 4 + g owns queries [128 (g / 2), +128) and columns
+//     [64 (g % 2), +64) of d of dQ (accumulators in registers).  One key
+//     block behind, it reads the K operand of that block (key on the
+//     contraction index) with ds_read_b64_tr_b16 -- each fragment feeds four
+//     products, one per query group -- and dS straight from the slabs, each
+//     slab feeding two products (every slab is read by two gradient waves,
+//     not four);
 //   * K blocks rotate through four LDS buffers (score waves read block p,
 //     gradient waves block p - 1, the copies of block p + 1, issued one
 //     phase earlier, complete before the phase's barrier, and direct-to-LDS
@@ -199,32 +201,37 @@ __device__ __forceinline__ void zero_step(unsigned char* smem, int dbuf, int s, 
                 make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Gradient role: dQ[:, 32 g .. 32 g + 31] += dS K for the block's 32 keys;
-// the second step's operands are read before the first step's products.
-// ob0 / ob1: the lane's transposing-read offsets for rows 4 h + (l % 16) / 4
-// and that + 8 (rows 16 t + ... share their swizzle).  stage(t) issues part
-// of a later block's copies after step t's products, so that the copies never
-// pile up in the memory pipeline in front of this wave's work.
+// Gradient role: for queries [128 qs, 128 qs + 128) (query groups 4 qs ..
+// 4 qs + 3) and d columns [64 ds, 64 ds + 64) (d tiles 2 ds, 2 ds + 1),
+// dQ += dS K for the block's 32 keys: per 16-key step two K operands
+// (transposing reads; ob0 / ob1: the lane's offsets for rows 4 h + (l % 16) / 4
+// and that + 8, rows 16 t + ... sharing their swizzle) and four dS slabs,
+// eight products.  Both steps' operands are read before the first step's
+// products.  stage(t) issues part of a later block's copies after step t's
+// products, so that the copies never pile up in the memory pipeline in front
+// of this wave's work.
 template <typename E, typename Stage>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, int dbuf,
-                                          f32x16_t (&acc)[QG], int ob0, int ob1, int l,
-                                          Stage&& stage) {
+                                          f32x16_t (&acc)[4][2], const int (&ob0)[2],
+                                          const int (&ob1)[2], int qs, int l, Stage&& stage) {
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
-    const unsigned char* k0p = sK + ob0;
-    const unsigned char* k1p = sK + ob1;
     const unsigned char* sl = smem + OFF_DS + dbuf * DSB + l * 16;
-    v16x8_t bK[2], aS[2][QG];
+    v16x8_t bK[2][2], aS[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        bK[t] = tr16_pair(k0p + 16 * ROWB * t, k1p + 16 * ROWB * t);
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) aS[t][qg] = lds_b128(sl + (t * QG + qg) * SLAB);
+        for (int dt = 0; dt < 2; ++dt)
+            bK[t][dt] = tr16_pair(sK + ob0[dt] + 16 * ROWB * t, sK + ob1[dt] + 16 * ROWB * t);
+#pragma unroll
+        for (int qg = 0; qg < 4; ++qg) aS[t][qg] = lds_b128(sl + (t * QG + 4 * qs + qg) * SLAB);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
 #pragma unroll
-        for (int qg = 0; qg < QG; ++qg) acc[qg] = E::mma(aS[t][qg], bK[t], acc[qg]);
+        for (int qg = 0; qg < 4; ++qg)
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) acc[qg][dt] = E::mma(aS[t][qg], bK[t][dt], acc[qg][dt]);
         stage(t);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -306,14 +313,23 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         return;
     }
 
-    f32x16_t acc[QG];
+    // gradient wave r4: query half qs, d half ds
+    const int qs = r4 >> 1, ds = r4 & 1;
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < QG; ++i) acc[i] = f32x16_t{};
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
     const TileCopier<BK, NWAVE / 2> cp(r4, l);
     const uint32_t lds0 = lds_addr(smem);
-    const int g2 = (l >> 4) & 1, colb = 64 * r4 + 32 * g2 + 8 * (l & 3);
-    const int x = 4 * h + ((l & 15) >> 2);
-    const int ob0 = tile_off(x, colb), ob1 = tile_off(x + 8, colb);
+    int ob0[2], ob1[2];
+    {
+        const int g2 = (l >> 4) & 1, x = 4 * h + ((l & 15) >> 2);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const int colb = 64 * (2 * ds + dt) + 32 * g2 + 8 * (l & 3);
+            ob0[dt] = tile_off(x, colb);
+            ob1[dt] = tile_off(x + 8, colb);
+        }
+    }
     for (int p = 0; p <= nblk; ++p) {
         // copies of block p + 2 first; block p + 1's (issued one phase ago)
         // must have landed by the barrier, these may stay in flight.  Past
@@ -329,7 +345,7 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         };
         static_assert(TileCopier<BK, NWAVE / 2>::SLICES == 2, "one slice per 16-key step");
         if (p >= 1) {
-            grad_step<E>(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, l, stage);
+            grad_step<E>(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, qs, l, stage);
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) stage(j);
@@ -341,15 +357,18 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         __syncthreads();
     }
 
-    // epilogue: acc[qg] holds dQ for queries q0 + 32 qg + 8 (r / 4) + 4 h + r % 4,
-    // column 32 g + n
+    // epilogue: acc[qg][dt] holds dQ for queries q0 + 32 (4 qs + qg) + 8 (r / 4) +
+    // 4 h + r % 4, column 32 (2 ds + dt) + n
     float* out = dqa + hoff;
 #pragma unroll
-    for (int qg = 0; qg < QG; ++qg)
+    for (int qg = 0; qg < 4; ++qg)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int qq = q0 + 32 * qg + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (qq < N) out[(long long)qq * D + 32 * r4 + n] = acc[qg][r];
+            const int qq = q0 + 32 * (4 * qs + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (qq < N)
+#pragma unroll
+                for (int dt = 0; dt < 2; ++dt)
+                    out[(long long)qq * D + 32 * (2 * ds + dt) + n] = acc[qg][dt][r];
         }
 }
 
