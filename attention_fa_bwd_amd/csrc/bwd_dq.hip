@@ -67,17 +67,15 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
                                            int k0, int qa, int N, float sc,
                                            const float (&Lq)[2], const float (&Dq)[2],
                                            const v16x8_t (&qt)[2][8], const v16x8_t (&gt)[2][8],
-                                           const int (&so)[8], int s, int l) {
+                                           const int (&so)[8], const v16x8_t (&bD)[2],
+                                           const v16x8_t& ones, int s, int l) {
     const int h = l >> 5;
     const unsigned char* sK = smem + OFF_K + kbuf * TILE;
     const unsigned char* sV = smem + OFF_V + vbuf * TILE;
     unsigned char* sS = smem + OFF_DS + dbuf * DSB;
     // dS = P (dP - D), packed, into the group's two slabs; grouped by
     // operation so that dependent instructions stand sixteen apart
-    auto finish = [&](f32x16_t& P, f32x16_t& dP, float Dg, int g) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) dP[e] -= Dg;
-        __builtin_amdgcn_sched_barrier(0);
+    auto finish = [&](f32x16_t& P, const f32x16_t& dP, int g) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) P[e] *= dP[e];
         __builtin_amdgcn_sched_barrier(0);
@@ -88,8 +86,10 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
                            E::pack2(P[8 * t + 4], P[8 * t + 5]),
                            E::pack2(P[8 * t + 6], P[8 * t + 7]));
     };
-    f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{}, dP0 = f32x16_t{}, dP1 = f32x16_t{};
+    f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{}, dP0, dP1;
     if (MASK) {
+        dP0 = mfma(ones, bD[0], f32x16_t{});
+        dP1 = mfma(ones, bD[1], f32x16_t{});
 #pragma unroll
         for (int dk = 0; dk < 8; ++dk) {
             const v16x8_t a = lds_b128(sK + so[dk]);
@@ -119,8 +119,8 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
         };
         expm(S0, qa, Lq[0]);
         expm(S1, qa + 32, Lq[1]);
-        finish(S0, dP0, Dq[0], 0);
-        finish(S1, dP1, Dq[1], 1);
+        finish(S0, dP0, 0);
+        finish(S1, dP1, 1);
         return;
     }
     // Operand u = 0..15 (K fragment u, then V fragment u - 8) sits in slot
@@ -169,6 +169,9 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
             }
         }
     };
+    // dP starts at -D: one product per group broadcasts the lane's value
+    dP0 = mfma(ones, bD[0], f32x16_t{});
+    dP1 = mfma(ones, bD[1], f32x16_t{});
     scale2(0);
     scale2(1);
 #pragma unroll
@@ -186,8 +189,8 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int kbuf, int vb
         if (2 * j + 3 < 16) scale2(2 * j + 3);
         __builtin_amdgcn_sched_barrier(0);
     }
-    finish(S0, dP0, Dq[0], 0);
-    finish(S1, dP1, Dq[1], 1);
+    finish(S0, dP0, 0);
+    finish(S1, dP1, 1);
 }
 
 // Score role, a key block wholly above this wave's queries (causal): dS = 0.
@@ -293,6 +296,21 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
         int so[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
+        // Starting value -D of the dP accumulators, made by one product per
+        // group: A is 1 on k-slots 0..2 (lanes of half 0), B holds -D of the
+        // lane's query split into three bf16 terms on those k-slots (about
+        // 2^-26 relative), so the product broadcasts -D down the key rows.
+        const v16x8_t ones = as_v16x8(h ? make_uint4(0, 0, 0, 0) : make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
+        v16x8_t bD[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float u = -Dq[g];
+            const float hi = (float)(__bf16)u;
+            const float r1 = u - hi;
+            const float mid = (float)(__bf16)r1;
+            bD[g] = as_v16x8(h ? make_uint4(0, 0, 0, 0)
+                               : make_uint4(pack_bf16x2(hi, mid), pack_bf16x2(r1 - mid, 0.f), 0, 0));
+        }
         // blocks needing no mask for any of this wave's queries
         const int full = CAUSAL ? min(qw / BK, N / BK) : N / BK;
         for (int p = 0; p <= nblk; ++p) {
@@ -302,10 +320,10 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
                     zero_step(smem, p & 1, r4, l);
                 else if (p < full)
                     score_step<E, false, CAUSAL>(smem, p % NKB, p % NVB, p & 1, k0, qa, N, sc, Lq,
-                                                 Dq, qt, gt, so, r4, l);
+                                                 Dq, qt, gt, so, bD, ones, r4, l);
                 else
                     score_step<E, true, CAUSAL>(smem, p % NKB, p % NVB, p & 1, k0, qa, N, sc, Lq,
-                                                Dq, qt, gt, so, r4, l);
+                                                Dq, qt, gt, so, bD, ones, r4, l);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
