@@ -251,8 +251,9 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
-    const int head = work / nkb;
-    const int k0 = (work % nkb) * BC;  // heaviest key blocks first under the causal mask
+    int head = work / nkb, kblk = work % nkb;
+    if (CAUSAL) heavy_first_work(work, gridDim.x, nkb, head, kblk);  // heaviest (first) key blocks first
+    const int k0 = kblk * BC;
     const long long hoff = (long long)head * N * D;
     const e16_t* Qh = Q + hoff;
     const e16_t* dOh = dO + hoff;

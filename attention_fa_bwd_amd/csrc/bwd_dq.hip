@@ -248,8 +248,11 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
-    const int head = work / nqb;
-    const int qblk = CAUSAL ? nqb - 1 - work % nqb : work % nqb;  // heaviest first
+    int head = work / nqb, qblk = work % nqb;
+    if (CAUSAL) {  // heaviest (last) query blocks first
+        heavy_first_work(work, gridDim.x, nqb, head, qblk);
+        qblk = nqb - 1 - qblk;
+    }
     const int q0 = qblk * BQ;
     const long long hoff = (long long)head * N * D;
     const e16_t* Kh = K + hoff;

@@ -232,5 +232,24 @@ __device__ __forceinline__ int xcd_work_item(int bid, int nwork) {
     return (nwork % 8 == 0) ? (bid % 8) * (nwork / 8) + bid / 8 : bid;
 }
 
+// Causal work item -> (head, rank of its block by work, 0 the heaviest), the
+// heaviest blocks first.  When each XCD's contiguous share of work items
+// holds whole pairs of heads, the two heads of a pair alternate (rank 0 of
+// head 2p, of head 2p + 1, then rank 1 of each, ...): with several heads per
+// share run one after the other, the last head's heavy blocks would start
+// after the others' light ones and leave the share's CUs idle at its end.
+__device__ __forceinline__ void heavy_first_work(int work, int nwork, int nb, int& head,
+                                                 int& rank) {
+    const bool pairs = nwork % 8 == 0 && (nwork / 8) % (2 * nb) == 0;
+    if (pairs) {
+        const int r = work % (2 * nb);
+        head = 2 * (work / (2 * nb)) + (r & 1);
+        rank = r >> 1;
+    } else {
+        head = work / nb;
+        rank = work % nb;
+    }
+}
+
 }  // namespace mf
 }  // namespace fa

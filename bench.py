@@ -7,7 +7,9 @@ over one batch of synthetic inputs already resident in HBM.  The forward that pr
 L runs once before timing and is not timed.
 
 Workload (default): B=1, H=32, N=8192, d=128, bf16, non-causal; the causal
-variant of the same shape is timed too and reported under "causal".
+variant of the same shape is timed too and reported under "causal", and the
+same step is timed on the two other full-size workloads (B=4 H=16 N=4000 with
+Q scaled by 4, and B=1 H=8 N=32768, both causal) under "other_workloads".
 FLOPs per step: 10*B*H*N^2*d, halved under the causal mask.
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
@@ -44,7 +46,10 @@ def parse():
                    choices=["h8_n1024_d64_bf16", "h32_n8192_d128_bf16",
                             "b4_h16_n4000_d128_bf16_q4", "h8_n32768_d128_bf16"])
     p.add_argument("--causal", action="store_true", help="primary line is the causal run")
-    p.add_argument("--no-extra", action="store_true", help="skip the second causal mode")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the second causal mode and the other workloads")
+    p.add_argument("--no-other", action="store_true",
+                   help="skip the other workloads (both causal modes of the main one still run)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--calibrate-copy", action="store_true",
@@ -263,6 +268,32 @@ def cpu_baseline(wl, causal: bool, budget_s: float):
             "host": f"{len(os.sched_getaffinity(0))} CPUs usable of {os.cpu_count()}, {model}"}
 
 
+def other_workload(wl, args):
+    """One backward step timed on another workload, in each of its causal modes."""
+    import numpy as np
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    import seeded_inputs as si
+    inp = si.draw(wl)
+    up = [torch.from_numpy(inp.bits[n].view(np.int16)).view(torch.bfloat16).cuda()
+          for n in ("Q", "K", "V", "dO")]
+    out = {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "modes": []}
+    for causal in wl.causal:
+        o, L = fa.forward(up[0], up[1], up[2], wl.scale, causal)
+        torch.cuda.synchronize()
+        r = gpu_time(wl, causal, args.steps, args.warmup, (*up, o, L))
+        tf = wl.flops(causal) / (r["ms_per_step"] * 1e-3) / 1e12
+        out["modes"].append({"causal": causal, "ms_per_step": round(r["ms_per_step"], 4),
+                             "tflops": round(tf, 3),
+                             "pct_bf16_peak": round(100.0 * tf / PEAK_BF16_TFLOPS, 2),
+                             "split_ms": {k: round(v, 4) for k, v in r["kernel_ms"].items()}})
+        del o, L
+    del up
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -355,6 +386,11 @@ def main():
             "split_ms": {k: round(v, 4) for k, v in other["kernel_ms"].items()},
             "kernels": other["kernels"], "forward": other["forward"],
             "recompute_L": other["recompute_L"], "forward_backward": other["forward_backward"]}
+    if not (args.no_extra or args.no_other) and args.workload == "h32_n8192_d128_bf16":
+        # the two other full-size workloads (their own causal modes), the
+        # same timed step; context beside the line, not its value
+        line["other_workloads"] = [other_workload(si.WORKLOADS[n], args)
+                                   for n in ("b4_h16_n4000_d128_bf16_q4", "h8_n32768_d128_bf16")]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(wl, args.causal, args.cpu_seconds)
     else:
