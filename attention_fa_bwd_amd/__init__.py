@@ -88,14 +88,27 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def _ptr(t: torch.Tensor, dtype=None) -> int:
+def _ptr(t: torch.Tensor, dtype=None, ref=None) -> int:
     if not t.is_cuda:
         raise ValueError("tensor must live on the GPU")
+    if ref is not None and t.device != ref.device:
+        raise ValueError(f"tensors on different devices: {t.device} and {ref.device}")
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"expected {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+def _ptrs(ref, *specs):
+    """Device addresses for (tensor, dtype, shape) triples, after the checks the
+    C-ABI cannot make: first every shape against the one the call's sizes
+    imply (a smaller buffer would be read or written out of bounds), then
+    device (that of ``ref``), contiguity and element type."""
+    for t, _, shape in specs:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return [_ptr(t, dtype, ref) for t, dtype, _ in specs]
 
 
 def _stream(stream) -> int:
@@ -115,67 +128,71 @@ def _shape(t: torch.Tensor):
     return tuple(int(x) for x in t.shape)
 
 
+def _sizes(t):
+    B, H, N, d = _shape(t)
+    return (B, H, N, d), (B, H, N)
+
+
 def fa_fwd_lse(q, k, v, o, L, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, d = _shape(q)
-    dt = _dtype_code(q)
-    rc = load().fa_fwd_lse(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
-                           _ptr(o, q.dtype), _ptr(L, torch.float32), B, H, N, d,
-                           float(scale), int(bool(causal)), _stream(stream))
+    s4, s3 = _sizes(q)
+    e = q.dtype
+    ptrs = _ptrs(q, (q, e, s4), (k, e, s4), (v, e, s4), (o, e, s4), (L, torch.float32, s3))
+    rc = load().fa_fwd_lse(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                           _stream(stream))
     _check("fa_fwd_lse", rc)
 
 
 def fa_lse(q, k, L, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, d = _shape(q)
-    dt = _dtype_code(q)
-    rc = load().fa_lse(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(L, torch.float32),
-                       B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    s4, s3 = _sizes(q)
+    ptrs = _ptrs(q, (q, q.dtype, s4), (k, q.dtype, s4), (L, torch.float32, s3))
+    rc = load().fa_lse(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                       _stream(stream))
     _check("fa_lse", rc)
 
 
 def fa_bwd_preprocess(o, do, D, dq_accum, stream=None) -> None:
-    B, H, N, d = _shape(o)
-    dt = _dtype_code(o)
-    rc = load().fa_bwd_preprocess(dt, _ptr(o, o.dtype), _ptr(do, o.dtype),
-                                  _ptr(D, torch.float32), _ptr(dq_accum, torch.float32),
-                                  B, H, N, d, _stream(stream))
+    s4, s3 = _sizes(o)
+    ptrs = _ptrs(o, (o, o.dtype, s4), (do, o.dtype, s4), (D, torch.float32, s3),
+                 (dq_accum, torch.float32, s4))
+    rc = load().fa_bwd_preprocess(_dtype_code(o), *ptrs, *s4, _stream(stream))
     _check("fa_bwd_preprocess", rc)
 
 
+def _bwd_inputs(q, k, v, do, L, D):
+    s4, s3 = _sizes(q)
+    e, f = q.dtype, torch.float32
+    return [(q, e, s4), (k, e, s4), (v, e, s4), (do, e, s4), (L, f, s3), (D, f, s3)]
+
+
 def fa_bwd(q, k, v, do, L, D, dq_accum, dk, dv, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, d = _shape(q)
-    dt = _dtype_code(q)
-    rc = load().fa_bwd(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
-                       _ptr(do, q.dtype), _ptr(L, torch.float32), _ptr(D, torch.float32),
-                       _ptr(dq_accum, torch.float32), _ptr(dk, q.dtype), _ptr(dv, q.dtype),
-                       B, H, N, d, float(scale), int(bool(causal)), _stream(stream))
+    s4, _ = _sizes(q)
+    ptrs = _ptrs(q, *_bwd_inputs(q, k, v, do, L, D), (dq_accum, torch.float32, s4),
+                 (dk, q.dtype, s4), (dv, q.dtype, s4))
+    rc = load().fa_bwd(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                       _stream(stream))
     _check("fa_bwd", rc)
 
 
 def fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, d = _shape(q)
-    dt = _dtype_code(q)
-    rc = load().fa_bwd_dkdv(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
-                            _ptr(do, q.dtype), _ptr(L, torch.float32), _ptr(D, torch.float32),
-                            _ptr(dk, q.dtype), _ptr(dv, q.dtype), B, H, N, d, float(scale),
-                            int(bool(causal)), _stream(stream))
+    s4, _ = _sizes(q)
+    ptrs = _ptrs(q, *_bwd_inputs(q, k, v, do, L, D), (dk, q.dtype, s4), (dv, q.dtype, s4))
+    rc = load().fa_bwd_dkdv(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                            _stream(stream))
     _check("fa_bwd_dkdv", rc)
 
 
 def fa_bwd_dq(q, k, v, do, L, D, dq_accum, scale: float, causal: bool, stream=None) -> None:
-    B, H, N, d = _shape(q)
-    dt = _dtype_code(q)
-    rc = load().fa_bwd_dq(dt, _ptr(q, q.dtype), _ptr(k, q.dtype), _ptr(v, q.dtype),
-                          _ptr(do, q.dtype), _ptr(L, torch.float32), _ptr(D, torch.float32),
-                          _ptr(dq_accum, torch.float32), B, H, N, d, float(scale),
-                          int(bool(causal)), _stream(stream))
+    s4, _ = _sizes(q)
+    ptrs = _ptrs(q, *_bwd_inputs(q, k, v, do, L, D), (dq_accum, torch.float32, s4))
+    rc = load().fa_bwd_dq(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                          _stream(stream))
     _check("fa_bwd_dq", rc)
 
 
 def fa_bwd_convert_dq(dq_accum, dq, scale: float, stream=None) -> None:
-    B, H, N, d = _shape(dq)
-    dt = _dtype_code(dq)
-    rc = load().fa_bwd_convert_dq(dt, _ptr(dq_accum, torch.float32), _ptr(dq, dq.dtype),
-                                  B, H, N, d, float(scale), _stream(stream))
+    s4, _ = _sizes(dq)
+    ptrs = _ptrs(dq, (dq_accum, torch.float32, s4), (dq, dq.dtype, s4))
+    rc = load().fa_bwd_convert_dq(_dtype_code(dq), *ptrs, *s4, float(scale), _stream(stream))
     _check("fa_bwd_convert_dq", rc)
 
 

@@ -106,6 +106,36 @@ def test_binding_rejects_cpu_tensors():
         fa.forward(x, x, x, 0.25, False)
 
 
+def test_binding_checks_every_shape_before_the_library():
+    """The C-ABI sees only pointers and (B, H, N, d): a smaller tensor would be
+    read or written out of bounds, so the binding compares every shape with the
+    one the sizes imply first."""
+    import torch
+    B, H, N, d = 1, 2, 8, 16
+    x4 = torch.zeros(B, H, N, d, dtype=torch.bfloat16)
+    f3 = torch.zeros(B, H, N)
+    f4 = torch.zeros(B, H, N, d)
+    short = torch.zeros(B, H, N - 1, d, dtype=torch.bfloat16)
+    bad3 = torch.zeros(B, H, N + 1)
+    bad4 = torch.zeros(B, H, N, d + 1)
+    cases = [
+        lambda: fa.fa_fwd_lse(x4, short, x4, x4, f3, 0.25, False),
+        lambda: fa.fa_fwd_lse(x4, x4, x4, x4, bad3, 0.25, False),
+        lambda: fa.fa_lse(x4, short, f3, 0.25, True),
+        lambda: fa.fa_bwd_preprocess(x4, short, f3, f4),
+        lambda: fa.fa_bwd_preprocess(x4, x4, f3, bad4),
+        lambda: fa.fa_bwd(x4, x4, short, x4, f3, f3, f4, x4, x4, 0.25, False),
+        lambda: fa.fa_bwd(x4, x4, x4, x4, f3, bad3, f4, x4, x4, 0.25, False),
+        lambda: fa.fa_bwd(x4, x4, x4, x4, f3, f3, f4, x4, short, 0.25, False),
+        lambda: fa.fa_bwd_dkdv(x4, x4, x4, short, f3, f3, x4, x4, 0.25, True),
+        lambda: fa.fa_bwd_dq(x4, x4, x4, x4, f3, f3, bad4, 0.25, True),
+        lambda: fa.fa_bwd_convert_dq(bad4, x4, 0.25),
+    ]
+    for i, call in enumerate(cases):
+        with pytest.raises(ValueError, match="expected shape"):
+            call()
+
+
 def _sources(*dirs, exts=(".py", ".hip", ".hpp", ".h", ".c", ".cpp")):
     for d in dirs:
         for base, _, files in os.walk(os.path.join(ROOT, d)):
