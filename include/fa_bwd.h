@@ -29,8 +29,10 @@
  *              the attention calls return FA_EINVAL otherwise (the
  *              convert step only multiplies by it and takes any value).
  *   Pointers   device pointers (hipMalloc'd or equivalent), owned by the
- *              caller, at least 16-byte aligned.  Outputs must not alias
- *              inputs.  The library allocates nothing and keeps no mutable
+ *              caller, at least 16-byte aligned, each to a buffer holding at
+ *              least the elements its layout implies for the call's B, H, N
+ *              and d (the library cannot check this: a smaller buffer is read
+ *              or written out of bounds).  Outputs must not alias inputs.  The library allocates nothing and keeps no mutable
  *              global state; calls on different streams may run concurrently
  *              as long as their buffers are disjoint.
  *   Stream     `stream` is a hipStream_t passed as void*; NULL is the null
