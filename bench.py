@@ -103,6 +103,14 @@ def calibrate_copy():
 KERNEL_FLOP_FACTOR = {"fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
 
 
+def hbm_kernel_bytes(wl) -> dict:
+    """Algorithmic HBM bytes per launch of the two streaming steps (16-bit
+    elements, d = 128: the preprocess leaves dq_accum to the dQ pass)."""
+    rows = wl.B * wl.H * wl.N
+    return {"fa_bwd_preprocess": rows * wl.d * 2 * 2 + rows * 4,   # read O, dO; write D
+            "fa_bwd_convert_dq": rows * wl.d * (4 + 2)}           # read dq_accum; write dQ
+
+
 def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     import torch
 
@@ -330,6 +338,12 @@ def main():
             r["kernels"][name] = {"avg_launch_ms": round(ms, 4), "flop_per_launch": kflop,
                                   "achieved": round(kflop / (ms * 1e-3) / 1e12, 3),
                                   "frac": round(kflop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        for name, nbytes in hbm_kernel_bytes(wl).items():
+            ms = r["kernel_ms"][name]
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            r["kernels"][name] = {"avg_launch_ms": round(ms, 4), "bytes_per_launch": nbytes,
+                                  "achieved_gbs": round(gbs, 1),
+                                  "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         fms = forward_time(wl, causal, (up["Q"], up["K"], up["V"]))
         ffl = 0.4 * flops  # 4·B·H·N²·d (×½ causal)
         r["forward"] = {"ms": round(fms, 4), "tflops": round(ffl / (fms * 1e-3) / 1e12, 3),
