@@ -33,7 +33,7 @@ _vp, _i, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
 _SIGS = {
     "fa_fwd_lse": [_i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_lse": [_i, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
-    "fa_bwd_preprocess": [_i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp],
+    "fa_bwd_preprocess": [_i, _vp, _vp, _vp, _i, _i, _i, _i, _vp],
     "fa_bwd": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_dkdv": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_dq": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
@@ -150,10 +150,9 @@ def fa_lse(q, k, L, scale: float, causal: bool, stream=None) -> None:
     _check("fa_lse", rc)
 
 
-def fa_bwd_preprocess(o, do, D, dq_accum, stream=None) -> None:
+def fa_bwd_preprocess(o, do, D, stream=None) -> None:
     s4, s3 = _sizes(o)
-    ptrs = _ptrs(o, (o, o.dtype, s4), (do, o.dtype, s4), (D, torch.float32, s3),
-                 (dq_accum, torch.float32, s4))
+    ptrs = _ptrs(o, (o, o.dtype, s4), (do, o.dtype, s4), (D, torch.float32, s3))
     rc = load().fa_bwd_preprocess(_dtype_code(o), *ptrs, *s4, _stream(stream))
     _check("fa_bwd_preprocess", rc)
 
@@ -224,7 +223,7 @@ def backward(q, k, v, o, do, L, scale: float, causal: bool, stream=None, workspa
     else:
         D, dq_accum = workspace
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    fa_bwd_preprocess(o, do, D, dq_accum, stream)
+    fa_bwd_preprocess(o, do, D, stream)
     fa_bwd(q, k, v, do, L, D, dq_accum, dk, dv, scale, causal, stream)
     fa_bwd_convert_dq(dq_accum, dq, scale, stream)
     return dq, dk, dv

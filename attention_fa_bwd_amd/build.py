@@ -20,8 +20,6 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # packed fp32 VALU forms are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # fp32 atomicAdd lowers to the hardware global_atomic_add_f32
-    "-munsafe-fp-atomics",
     "-Wno-unused-command-line-argument",
 ]
 

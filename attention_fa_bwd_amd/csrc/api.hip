@@ -51,6 +51,23 @@ int device_ready() {
     return hip_status(hipGetDevice(&dev));
 }
 
+// The two passes of the backward, on the matrix cores where they apply.
+hipError_t launch_dkdv(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+                       const float* L, const float* D, void* dK, void* dV, fa::Shape s,
+                       float scale, bool causal, hipStream_t st) {
+    return matrix_core(dtype, s.d)
+               ? fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal, st)
+               : fa::launch_bwd_dkdv_simt(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal, st);
+}
+
+hipError_t launch_dq(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+                     const float* L, const float* D, float* dq_accum, fa::Shape s, float scale,
+                     bool causal, hipStream_t st) {
+    return matrix_core(dtype, s.d)
+               ? fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
+               : fa::launch_bwd_dq_simt(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,13 +99,13 @@ int fa_lse(int dtype, const void* Q, const void* K, float* L, int B, int H, int 
     return hip_status(fa::launch_lse(dtype, Q, K, L, s, scale, causal != 0, (hipStream_t)stream));
 }
 
-int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D, float* dq_accum,
-                      int B, int H, int N, int d, void* stream) {
-    int rc = check(dtype, B, H, N, d, {O, dO, D, dq_accum});
+int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D, int B, int H, int N,
+                      int d, void* stream) {
+    int rc = check(dtype, B, H, N, d, {O, dO, D});
     if (rc != FA_OK) return rc;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_preprocess(dtype, O, dO, D, dq_accum, fa::Shape{B, H, N, d},
-                                            (hipStream_t)stream));
+    return hip_status(
+        fa::launch_preprocess(dtype, O, dO, D, fa::Shape{B, H, N, d}, (hipStream_t)stream));
 }
 
 int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* dO,
@@ -100,16 +117,10 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     const hipStream_t st = (hipStream_t)stream;
-    // one kernel per (dtype, head dim): matrix cores for 16-bit d=128, vector ALUs otherwise
-    if (matrix_core(dtype, d)) {
-        int rc2 = hip_status(fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, s, scale,
-                                                    causal != 0, st));
-        if (rc2 != FA_OK) return rc2;
-        return hip_status(fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, s, scale,
-                                                   causal != 0, st));
-    }
-    return hip_status(fa::launch_bwd_simt(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale,
-                                          causal != 0, st));
+    // the two passes: dQ (query-outer), then dK/dV (key-outer)
+    rc = hip_status(launch_dq(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal != 0, st));
+    if (rc != FA_OK) return rc;
+    return hip_status(launch_dkdv(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal != 0, st));
 }
 
 int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const void* dO,
@@ -118,10 +129,9 @@ int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const vo
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dK, dV});
     if (rc != FA_OK) return rc;
     if (!scale_ok(scale)) return FA_EINVAL;
-    if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d},
-                                               scale, causal != 0, (hipStream_t)stream));
+    return hip_status(launch_dkdv(dtype, Q, K, V, dO, L, D, dK, dV, fa::Shape{B, H, N, d}, scale,
+                                  causal != 0, (hipStream_t)stream));
 }
 
 int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V, const void* dO,
@@ -130,10 +140,9 @@ int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V, const void
     int rc = check(dtype, B, H, N, d, {Q, K, V, dO, L, D, dq_accum});
     if (rc != FA_OK) return rc;
     if (!scale_ok(scale)) return FA_EINVAL;
-    if (!matrix_core(dtype, d)) return FA_EUNSUPPORTED;
     if ((rc = device_ready()) != FA_OK) return rc;
-    return hip_status(fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d},
-                                             scale, causal != 0, (hipStream_t)stream));
+    return hip_status(launch_dq(dtype, Q, K, V, dO, L, D, dq_accum, fa::Shape{B, H, N, d}, scale,
+                                causal != 0, (hipStream_t)stream));
 }
 
 int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ, int B, int H, int N, int d,

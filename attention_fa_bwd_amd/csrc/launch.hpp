@@ -7,8 +7,8 @@
 
 namespace fa {
 
-hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D,
-                             float* dq_accum, Shape s, hipStream_t st);
+hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D, Shape s,
+                             hipStream_t st);
 
 hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s,
                              float scale, hipStream_t st);
@@ -26,11 +26,14 @@ hipError_t launch_lse(int dtype, const void* Q, const void* K, float* L, Shape s
 hipError_t launch_lse_d128(int dtype, const void* Q, const void* K, float* L, Shape s,
                            float scale, bool causal, hipStream_t st);
 
-// Vector-ALU backward (fp32 FMA): every dtype and head dim.
-hipError_t launch_bwd_simt(int dtype, const void* Q, const void* K, const void* V,
-                           const void* dO, const float* L, const float* D, float* dq_accum,
-                           void* dK, void* dV, Shape s, float scale, bool causal,
-                           hipStream_t st);
+// Vector-ALU backward (fp32 FMA), every dtype and head dim: key-outer dK/dV
+// pass and query-outer dQ pass (dq_accum rows written once, unscaled).
+hipError_t launch_bwd_dkdv_simt(int dtype, const void* Q, const void* K, const void* V,
+                                const void* dO, const float* L, const float* D, void* dK,
+                                void* dV, Shape s, float scale, bool causal, hipStream_t st);
+hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const void* V,
+                              const void* dO, const float* L, const float* D, float* dq_accum,
+                              Shape s, float scale, bool causal, hipStream_t st);
 
 // Matrix-core backward, bf16 or fp16 (dtype), head dim 128: key-outer dK/dV
 // pass and query-outer dQ pass (dq_accum rows written once, unscaled).

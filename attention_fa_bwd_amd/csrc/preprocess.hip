@@ -2,9 +2,8 @@
 //
 // preprocess: D_i = sum_k O_ik dO_ik in fp32 (FA2 chapter 16, sec 16.1: the
 //   identity D_i = dO_i . O_i; sec 16.8 item 1: computed once before the main
-//   loop) and dq_accum := 0 where the main step accumulates into it (the
-//   vector-ALU path); the matrix-core dQ pass (16-bit elements, d = 128)
-//   writes every dq_accum row itself, so there the zeroing is skipped.
+//   loop).  dq_accum needs no clearing: the query-outer dQ pass writes every
+//   element of it.
 // convert:    dQ = scale * dq_accum, cast to the element type (sec 16.3: the
 //   separate kernel that applies the softmax scale to the fp32 buffer).
 //
@@ -15,11 +14,10 @@
 
 namespace fa {
 
-template <typename T, int D, bool ZERO>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ O,
                                                          const T* __restrict__ dO,
                                                          float* __restrict__ Dout,
-                                                         float* __restrict__ dqa,
                                                          long long rows) {
     constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte access
     constexpr int TPR = D / VEC;         // lanes per row
@@ -40,11 +38,6 @@ __global__ __launch_bounds__(256) void preprocess_kernel(const T* __restrict__ O
 #pragma unroll
         for (int m = TPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
         if (sub == 0) Dout[row] = acc;
-        if (ZERO) {
-            float4* z = reinterpret_cast<float4*>(dqa + off);
-#pragma unroll
-            for (int i = 0; i < VEC / 4; ++i) z[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
     }
 }
 
@@ -81,33 +74,29 @@ static unsigned grid_for(long long work, long long per_block) {
 }
 
 template <typename T, int D>
-static hipError_t pre_t(const void* O, const void* dO, float* Dv, float* dqa, Shape s,
-                        hipStream_t st) {
+static hipError_t pre_t(const void* O, const void* dO, float* Dv, Shape s, hipStream_t st) {
     constexpr int RPB = 256 / (D / (16 / (int)sizeof(T)));
-    // zeroing only where the main step accumulates (not 16-bit with d = 128)
-    constexpr bool ZERO = !(sizeof(T) == 2 && D == 128);
-    hipLaunchKernelGGL((preprocess_kernel<T, D, ZERO>), dim3(grid_for(s.rows(), RPB)), dim3(256),
-                       0, st, (const T*)O, (const T*)dO, Dv, dqa, s.rows());
+    hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3(grid_for(s.rows(), RPB)), dim3(256), 0,
+                       st, (const T*)O, (const T*)dO, Dv, s.rows());
     return hipGetLastError();
 }
 
 template <typename T>
-static hipError_t pre_d(const void* O, const void* dO, float* Dv, float* dqa, Shape s,
-                        hipStream_t st) {
+static hipError_t pre_d(const void* O, const void* dO, float* Dv, Shape s, hipStream_t st) {
     switch (s.d) {
-        case 16: return pre_t<T, 16>(O, dO, Dv, dqa, s, st);
-        case 32: return pre_t<T, 32>(O, dO, Dv, dqa, s, st);
-        case 64: return pre_t<T, 64>(O, dO, Dv, dqa, s, st);
-        case 128: return pre_t<T, 128>(O, dO, Dv, dqa, s, st);
+        case 16: return pre_t<T, 16>(O, dO, Dv, s, st);
+        case 32: return pre_t<T, 32>(O, dO, Dv, s, st);
+        case 64: return pre_t<T, 64>(O, dO, Dv, s, st);
+        case 128: return pre_t<T, 128>(O, dO, Dv, s, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D,
-                             float* dq_accum, Shape s, hipStream_t st) {
-    return dtype == DT_BF16  ? pre_d<bf16_t>(O, dO, D, dq_accum, s, st)
-           : dtype == DT_F16 ? pre_d<f16_t>(O, dO, D, dq_accum, s, st)
-                             : pre_d<float>(O, dO, D, dq_accum, s, st);
+hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D, Shape s,
+                             hipStream_t st) {
+    return dtype == DT_BF16  ? pre_d<bf16_t>(O, dO, D, s, st)
+           : dtype == DT_F16 ? pre_d<f16_t>(O, dO, D, s, st)
+                             : pre_d<float>(O, dO, D, s, st);
 }
 
 hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s, float scale,

@@ -128,7 +128,7 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     def step(evs=None):
         if evs:
             evs[0].record(stream)
-        fa.fa_bwd_preprocess(o, do, D, dqa, stream)
+        fa.fa_bwd_preprocess(o, do, D, stream)
         if evs:
             evs[1].record(stream)
         fa.fa_bwd_dq(q, k, v, do, L, D, dqa, scale, causal, stream)
@@ -230,7 +230,7 @@ def fwd_bwd_time(wl, causal: bool, inputs, reps: int = 5):
 
     def one():
         fa.fa_fwd_lse(q, k, v, o, L, wl.scale, causal, stream)
-        fa.fa_bwd_preprocess(o, do, D, dqa, stream)
+        fa.fa_bwd_preprocess(o, do, D, stream)
         fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, wl.scale, causal, stream)
         fa.fa_bwd_convert_dq(dqa, dq, wl.scale, stream)
 

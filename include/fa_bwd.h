@@ -6,12 +6,13 @@
  * dQ/dK/dV 的重计算".  Given Q, K, V, O, dO and the per-row logsumexp L of the
  * forward, the backward produces dQ, dK and dV without materialising the N x N
  * probability matrix: a preprocess computes D = rowsum(O * dO) (sec 16.1 and
- * sec 16.8 item 1), the main kernel runs key blocks outer and query blocks
+ * sec 16.8 item 1), the main step runs key blocks outer and query blocks
  * inner (sec 16.2), recomputes S = scale * Q K^T and P = exp(S - L) on chip
  * (sec 16.4), forms dS = P * (dP - D) and accumulates dV = P^T dO, dK = dS^T Q
- * per key block and dQ = dS K into an fp32 buffer (sec 16.3, the fp32
- * accumulation-buffer variant), and a convert step scales dQ and casts it
- * (sec 16.3 and 16.6).
+ * per key block, and dQ = dS K goes to an fp32 buffer (sec 16.3, the fp32
+ * accumulation-buffer variant) -- summed by a second, query-outer pass rather
+ * than by atomics (sec 16.3 weighs the two) -- and a convert step scales dQ and
+ * casts it (sec 16.3 and 16.6).
  *
  * Conventions shared by every entry point
  *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d] row-major
@@ -39,7 +40,7 @@
  *              stream.  Every call only enqueues work and returns; the caller
  *              synchronises.
  *   Sizes      B, H, N, d >= 1; B * H * N * d < 2^40; B and H < 65536.
- *              Supported head dims: d in {16, 32, 64, 128} for both dtypes.
+ *              Supported head dims: d in {16, 32, 64, 128} for every dtype.
  *   Errors     every call returns an fa_status_t.  Arguments are validated
  *              before any device work: FA_EINVAL for a NULL pointer, a
  *              non-positive or oversized dimension, an unknown dtype or a
@@ -100,31 +101,26 @@ int fa_lse(int dtype, const void* Q, const void* K, float* L,
 /*
  * fa_bwd_preprocess -- D_i = sum_k O_ik dO_ik with fp32 accumulation (FA2
  * chapter 16 sec 16.1, the identity D_i = dO_i . O_i, and sec 16.8 item 1:
- * computed once before the main loop), and dq_accum := 0 for the dtype /
- * head-dim pairs whose main step accumulates into it.
+ * computed once before the main loop).  dq_accum needs no clearing (fa_bwd
+ * writes every element of it), so this step touches D only.
  *   in : O, dO [B,H,N,d] dtype
- *   out: D [B,H,N] fp32 (written); dq_accum [B,H,N,d] fp32: zeroed, except
- *        for bf16 / fp16 with d = 128, where it is left untouched because
- *        the dQ pass (fa_bwd, fa_bwd_dq) writes every element
+ *   out: D [B,H,N] fp32 (every element written)
  */
-int fa_bwd_preprocess(int dtype, const void* O, const void* dO,
-                      float* D, float* dq_accum,
+int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D,
                       int B, int H, int N, int d, void* stream);
 
 /*
  * fa_bwd -- the main backward step (FA2 chapter 16 sec 16.2 loop order, sec
- * 16.6 skeleton): per (key block, head, batch) it recomputes S = scale Q K^T
- * and P = exp(S - L), forms dP = dO V^T and dS = P (dP - D), and accumulates
- * dV = P^T dO and dK = dS^T Q (dK multiplied by `scale` at write-out, sec
- * 16.6); under the causal mask, tiles wholly above the diagonal are skipped
- * (sec 16.8 item 2).  dQ = dS K, unscaled, ends up in the fp32 dq_accum buffer
- * (sec 16.3).
- *   bf16 / fp16, d = 128: two matrix-core passes, fa_bwd_dq then fa_bwd_dkdv;
- *                  dq_accum is overwritten, every output is bitwise
- *                  reproducible.
- *   other pairs:   one vector-ALU kernel that adds dQ partials into dq_accum
- *                  with fp32 atomics; dq_accum must hold zeros
- *                  (fa_bwd_preprocess) and its summation order varies.
+ * 16.6 skeleton): it recomputes S = scale Q K^T and P = exp(S - L), forms
+ * dP = dO V^T and dS = P (dP - D), and accumulates dV = P^T dO and dK = dS^T Q
+ * per key block (dK multiplied by `scale` at write-out, sec 16.6) and
+ * dQ = dS K (unscaled) per query block; under the causal mask, tiles wholly
+ * above the diagonal are skipped (sec 16.8 item 2).  It is fa_bwd_dq followed
+ * by fa_bwd_dkdv on the same stream.
+ *   One contract for every dtype and head dim: dq_accum is overwritten (its
+ *   prior contents are never read), no atomics are used, and dq_accum, dK
+ *   and dV are bitwise reproducible from call to call.  bf16 and fp16 with
+ *   d = 128 run on the matrix cores; the other pairs on the vector ALUs.
  *   in : Q, K, V, dO [B,H,N,d] dtype; L, D [B,H,N] fp32
  *   out: dq_accum [B,H,N,d] fp32 = sum_j dS_ij K_j (unscaled);
  *        dK, dV [B,H,N,d] dtype
@@ -136,18 +132,16 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V,
            void* stream);
 
 /*
- * fa_bwd_dkdv / fa_bwd_dq -- the two passes fa_bwd runs for bf16 and fp16 with
- * d = 128,
- * callable on their own (same arguments and layouts as fa_bwd).  FA2 chapter
- * 16 sec 16.3 weighs fp32 global atomics for dQ against a second kernel; on
- * MI355X the atomics measured too slow (about 340 G fp32 atomics/s), so dQ has
- * its own query-outer pass:
+ * fa_bwd_dkdv / fa_bwd_dq -- the two passes fa_bwd runs, callable on their
+ * own (same arguments and layouts as fa_bwd, every dtype and head dim).  FA2
+ * chapter 16 sec 16.3 weighs fp32 global atomics for dQ against a second
+ * kernel; on MI355X the atomics measured too slow (about 340 G fp32
+ * atomics/s), so dQ has its own query-outer pass:
  *   fa_bwd_dkdv: key blocks outer, query tiles inner (sec 16.2); recomputes S,
  *                P, dP, dS and accumulates dV = P^T dO, dK = scale dS^T Q.
  *   fa_bwd_dq:   query blocks outer, key blocks inner; recomputes S, P, dP, dS
  *                and accumulates dQ = dS K, written once (unscaled) into
  *                dq_accum -- no atomics, bitwise reproducible.
- * Other dtype / head-dim pairs return FA_EUNSUPPORTED (fa_bwd covers them).
  */
 int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V,
                 const void* dO, const float* L, const float* D,

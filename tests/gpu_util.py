@@ -59,7 +59,7 @@ def run_gpu(inp: si.Inputs, causal: bool, O=None, L=None):
     D = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
     dqa = torch.full((B, H, N, d), float("nan"), dtype=torch.float32, device="cuda")
     dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
-    fa.fa_bwd_preprocess(o, do, D, dqa)
+    fa.fa_bwd_preprocess(o, do, D)
     fa.fa_bwd(q, k, v, do, Lt, D, dqa, dk, dv, scale, causal)
     fa.fa_bwd_convert_dq(dqa, dq, scale)
     torch.cuda.synchronize()

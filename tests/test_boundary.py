@@ -72,7 +72,7 @@ def test_invalid_arguments_rejected_before_device_work():
         assert lib.fa_bwd(1, p, p, p, p, p, p, p, p, p, 1, 1, 8, 64, bad, 0, None) == fa.FA_EINVAL
         assert lib.fa_bwd_dkdv(1, p, p, p, p, p, p, p, p, 1, 1, 8, 128, bad, 0, None) == fa.FA_EINVAL
         assert lib.fa_bwd_dq(2, p, p, p, p, p, p, p, 1, 1, 8, 128, bad, 1, None) == fa.FA_EINVAL
-    assert lib.fa_bwd_preprocess(1, p, p, p, None, 1, 1, 8, 64, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_preprocess(1, p, p, None, 1, 1, 8, 64, None) == fa.FA_EINVAL
     assert lib.fa_bwd_convert_dq(0, None, p, 1, 1, 8, 64, 0.1, None) == fa.FA_EINVAL
 
 
@@ -83,20 +83,72 @@ def test_unsupported_head_dim(d):
     assert _bwd(lib, d=d) == fa.FA_EUNSUPPORTED
     assert lib.fa_fwd_lse(0, p, p, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_lse(1, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
-    assert lib.fa_bwd_preprocess(1, p, p, p, p, 1, 1, 8, d, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_bwd_preprocess(1, p, p, p, 1, 1, 8, d, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_bwd_convert_dq(1, p, p, 1, 1, 8, d, 0.1, None) == fa.FA_EUNSUPPORTED
 
 
-def test_split_passes_only_for_16bit_d128():
+def test_split_passes_validate_arguments():
     lib = fa.load()
     p = ALIGNED
     assert _bwd(lib, dtype=3) == fa.FA_EINVAL
-    for dtype, d in ((0, 128), (1, 64), (0, 16), (2, 64), (2, 32)):
-        assert lib.fa_bwd_dkdv(dtype, p, p, p, p, p, p, p, p, 1, 1, 8, d, 0.1, 0, None) == fa.FA_EUNSUPPORTED
-        assert lib.fa_bwd_dq(dtype, p, p, p, p, p, p, p, 1, 1, 8, d, 0.1, 1, None) == fa.FA_EUNSUPPORTED
     assert lib.fa_bwd_dkdv(1, p, None, p, p, p, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
     assert lib.fa_bwd_dq(1, p, p, p, p, p, p, None, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
-    assert lib.fa_bwd_dkdv(2, p, None, p, p, p, p, p, p, 1, 1, 8, 128, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_dkdv(2, p, None, p, p, p, p, p, p, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
+    assert lib.fa_bwd_dq(0, p, p, p, p, p, p, p, 1, 1, 8, 96, 0.1, 1, None) == fa.FA_EUNSUPPORTED
+    assert lib.fa_bwd_dkdv(0, p, p, p, p, p, p, p, p, 1, 1, 8, 8, 0.1, 1, None) == fa.FA_EUNSUPPORTED
+
+
+# Run in a child process: every entry point with valid arguments must return
+# FA_EHIP (and never crash) when no device is present.  The child first asks
+# the HIP runtime how many devices it sees and makes no call at all if there
+# is one, so the fake addresses below never reach a kernel.
+_NO_DEVICE_CHILD = r"""
+import ctypes, ctypes.util, json, sys
+lib = ctypes.CDLL(sys.argv[1])
+name = ctypes.util.find_library("amdhip64") or "/opt/rocm/lib/libamdhip64.so"
+hip = ctypes.CDLL(name)
+n = ctypes.c_int(0)
+rc = hip.hipGetDeviceCount(ctypes.byref(n))
+if rc == 0 and n.value > 0:
+    print(json.dumps({"device": True}))
+    sys.exit(0)
+p, f = ctypes.c_void_p(4096), ctypes.c_float
+lib.fa_last_hip_error.restype = ctypes.c_int
+out = {"device": False, "count_rc": rc}
+calls = {
+    "fa_fwd_lse": lambda d, t: lib.fa_fwd_lse(t, p, p, p, p, p, 1, 2, 40, d, f(0.125), 1, None),
+    "fa_lse": lambda d, t: lib.fa_lse(t, p, p, p, 1, 2, 40, d, f(0.125), 0, None),
+    "fa_bwd_preprocess": lambda d, t: lib.fa_bwd_preprocess(t, p, p, p, 1, 2, 40, d, None),
+    "fa_bwd": lambda d, t: lib.fa_bwd(t, p, p, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 1, None),
+    "fa_bwd_dkdv": lambda d, t: lib.fa_bwd_dkdv(t, p, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 0, None),
+    "fa_bwd_dq": lambda d, t: lib.fa_bwd_dq(t, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 1, None),
+    "fa_bwd_convert_dq": lambda d, t: lib.fa_bwd_convert_dq(t, p, p, 1, 2, 40, d, f(0.125), None),
+}
+for nm, call in calls.items():
+    for d in (16, 32, 64, 128):
+        for t in (0, 1, 2):
+            out[f"{nm}/d{d}/t{t}"] = [call(d, t), lib.fa_last_hip_error()]
+print(json.dumps(out))
+"""
+
+
+def test_every_entry_point_reports_no_device():
+    """Without a device every entry point returns FA_EHIP with the HIP error
+    recorded, for every dtype and head dim, before any launch."""
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", _NO_DEVICE_CHILD, fa.lib_path()],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    out = json.loads(r.stdout.strip().splitlines()[-1])
+    if out["device"]:
+        pytest.skip("a device is present; the no-device path cannot be exercised here")
+    results = {k: v for k, v in out.items() if "/" in k}
+    assert len(results) == 7 * 4 * 3
+    for k, (rc, hip_err) in results.items():
+        assert rc == fa.FA_EHIP, (k, rc)
+        assert hip_err != 0, k
 
 
 def test_binding_rejects_cpu_tensors():
@@ -122,8 +174,8 @@ def test_binding_checks_every_shape_before_the_library():
         lambda: fa.fa_fwd_lse(x4, short, x4, x4, f3, 0.25, False),
         lambda: fa.fa_fwd_lse(x4, x4, x4, x4, bad3, 0.25, False),
         lambda: fa.fa_lse(x4, short, f3, 0.25, True),
-        lambda: fa.fa_bwd_preprocess(x4, short, f3, f4),
-        lambda: fa.fa_bwd_preprocess(x4, x4, f3, bad4),
+        lambda: fa.fa_bwd_preprocess(x4, short, f3),
+        lambda: fa.fa_bwd_preprocess(x4, x4, bad3),
         lambda: fa.fa_bwd(x4, x4, short, x4, f3, f3, f4, x4, x4, 0.25, False),
         lambda: fa.fa_bwd(x4, x4, x4, x4, f3, bad3, f4, x4, x4, 0.25, False),
         lambda: fa.fa_bwd(x4, x4, x4, x4, f3, f3, f4, x4, short, 0.25, False),

@@ -176,28 +176,31 @@ def test_max_in_last_key_block():
     assert errs["o"] <= 1e-5
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_dk_dv_bitwise_repeatable(d):
-    """dK and dV never use atomics; dQ is reproducible on the matrix-core path
-    (d=128) and within tolerance where atomics reorder its sums (d=64)."""
-    gu.note(f"case repeatability d={d}")
-    inp = si.draw_custom(1, 4, 1024, d, "bf16", seed=1)
+REPEAT = [(d, dt) for d in (16, 32, 64, 128) for dt in ("fp32", "bf16", "fp16")]
+
+
+@pytest.mark.parametrize("d,dtype", REPEAT, ids=[f"{dt}-d{d}" for d, dt in REPEAT])
+def test_bitwise_repeatable(d, dtype):
+    """No path uses atomics: dq_accum, dQ, dK and dV are bitwise the same from
+    one call to the next, for every dtype and head dim."""
+    gu.note(f"case repeatability d={d} {dtype}")
+    inp = si.draw_custom(1, 4, 300, d, dtype, seed=1)
     a = gu.run_gpu(inp, True)
     b = gu.run_gpu(inp, True)
-    assert torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
-    if d == 128:
-        assert torch.equal(a["dq"], b["dq"])
-    else:
-        assert float((a["dq"].float() - b["dq"].float()).abs().max()) <= 1e-2 * float(a["dq"].float().abs().max())
+    for n in ("dq_accum", "dq", "dk", "dv"):
+        assert torch.equal(a[n], b[n]), n
+
+
+SPLIT = [(128, "bf16"), (128, "fp16"), (64, "bf16"), (16, "fp32"), (128, "fp32"), (32, "bf16")]
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_split_passes_equal_fa_bwd(causal):
-    """fa_bwd (bf16, d=128) is exactly fa_bwd_dq followed by fa_bwd_dkdv, and
-    both passes are bitwise reproducible (no atomics)."""
+@pytest.mark.parametrize("d,dtype", SPLIT, ids=[f"{dt}-d{d}" for d, dt in SPLIT])
+def test_split_passes_equal_fa_bwd(d, dtype, causal):
+    """fa_bwd is exactly fa_bwd_dq followed by fa_bwd_dkdv, on every path."""
     import attention_fa_bwd_amd as fa
-    gu.note(f"case split passes causal={causal}")
-    inp = si.draw_custom(1, 3, 700, 128, "bf16", seed=31)
+    gu.note(f"case split passes d={d} {dtype} causal={causal}")
+    inp = si.draw_custom(1, 3, 700, d, dtype, seed=31)
     out = gu.run_gpu(inp, causal)
     q, k, v, do, L, D = (out[n] for n in ("q", "k", "v", "do", "L", "D"))
     dqa = torch.full_like(out["dq_accum"], float("nan"))
@@ -207,6 +210,25 @@ def test_split_passes_equal_fa_bwd(causal):
     torch.cuda.synchronize()
     assert torch.equal(dqa, out["dq_accum"])
     assert torch.equal(dk, out["dk"]) and torch.equal(dv, out["dv"])
+
+
+@pytest.mark.parametrize("d,dtype", SPLIT, ids=[f"{dt}-d{d}" for d, dt in SPLIT])
+def test_dq_accum_overwritten(d, dtype):
+    """fa_bwd overwrites dq_accum: called twice on a buffer that holds the first
+    call's result (or large values), it gives the same bits, never a sum."""
+    import attention_fa_bwd_amd as fa
+    gu.note(f"case dq_accum overwrite d={d} {dtype}")
+    inp = si.draw_custom(2, 2, 260, d, dtype, seed=77)
+    out = gu.run_gpu(inp, False)
+    q, k, v, do, L, D = (out[n] for n in ("q", "k", "v", "do", "L", "D"))
+    dqa, dk, dv = out["dq_accum"].clone(), torch.empty_like(q), torch.empty_like(q)
+    fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, inp.wl.scale, False)
+    torch.cuda.synchronize()
+    assert torch.equal(dqa, out["dq_accum"])
+    dqa.fill_(1.0e6)
+    fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, inp.wl.scale, False)
+    torch.cuda.synchronize()
+    assert torch.equal(dqa, out["dq_accum"])
 
 
 # ------------------------------------------------------ full-size workloads

@@ -3,9 +3,8 @@
 * Calls only enqueue on the stream they are given, and calls on different
   streams with disjoint buffers may run concurrently: two independent
   backward problems issued alternately on two streams give the same results
-  as the same calls issued one problem after the other (bitwise where no
-  atomics are involved, within the tolerance where the vector-ALU path sums
-  dQ with atomics).
+  as the same calls issued one problem after the other, bitwise (no path
+  uses atomics).
 * Many heads: thousands of (b, h) pairs of a short sequence exercise the
   work-item decomposition of every kernel; sampled heads are compared with
   the oracle's plain definition."""
@@ -35,7 +34,7 @@ def _problem(inp, causal, stream):
     scale = inp.wl.scale
     calls = [
         lambda: fa.fa_fwd_lse(t["q"], t["k"], t["v"], t["o"], t["L"], scale, causal, stream),
-        lambda: fa.fa_bwd_preprocess(t["o"], t["do"], t["D"], t["dqa"], stream),
+        lambda: fa.fa_bwd_preprocess(t["o"], t["do"], t["D"], stream),
         lambda: fa.fa_bwd(t["q"], t["k"], t["v"], t["do"], t["L"], t["D"], t["dqa"], t["dk"],
                           t["dv"], scale, causal, stream),
         lambda: fa.fa_bwd_convert_dq(t["dqa"], t["dq"], scale, stream),
@@ -43,7 +42,7 @@ def _problem(inp, causal, stream):
     return t, calls
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 128), ("bf16", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp32", 16)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_two_streams_match_one(dtype, d, causal):
     gu.note(f"case two streams {dtype} d={d} causal={causal}")
@@ -66,15 +65,9 @@ def test_two_streams_match_one(dtype, d, causal):
         y()
     s1.synchronize()
     s2.synchronize()
-    exact = d == 128   # the matrix-core path: no atomics anywhere
-    for t, r, inp in ((ta, ref[0], ia), (tb, ref[1], ib)):
-        for n in ("o", "L", "dk", "dv"):
+    for t, r in ((ta, ref[0]), (tb, ref[1])):
+        for n in ("o", "L", "dq", "dk", "dv"):
             assert torch.equal(t[n], r[n]), n
-        if exact:
-            assert torch.equal(t["dq"], r["dq"])
-        else:
-            num = float((t["dq"].float() - r["dq"].float()).abs().max())
-            assert num <= 1e-2 * float(r["dq"].float().abs().max())
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
