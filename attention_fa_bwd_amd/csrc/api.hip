@@ -25,9 +25,9 @@ bool dtype_ok(int dtype) {
     return dtype == FA_DTYPE_F32 || dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16;
 }
 
-// The matrix-core kernels: 16-bit elements, head dim 128.
+// The matrix-core kernels: 16-bit elements, head dims 64 and 128.
 bool matrix_core(int dtype, int d) {
-    return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && d == 128;
+    return (dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_F16) && (d == 64 || d == 128);
 }
 
 bool head_dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -56,7 +56,7 @@ hipError_t launch_dkdv(int dtype, const void* Q, const void* K, const void* V, c
                        const float* L, const float* D, void* dK, void* dV, fa::Shape s,
                        float scale, bool causal, hipStream_t st) {
     return matrix_core(dtype, s.d)
-               ? fa::launch_bwd_dkdv_d128(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal, st)
+               ? fa::launch_bwd_dkdv_mfma(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal, st)
                : fa::launch_bwd_dkdv_simt(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal, st);
 }
 
@@ -64,7 +64,7 @@ hipError_t launch_dq(int dtype, const void* Q, const void* K, const void* V, con
                      const float* L, const float* D, float* dq_accum, fa::Shape s, float scale,
                      bool causal, hipStream_t st) {
     return matrix_core(dtype, s.d)
-               ? fa::launch_bwd_dq_d128(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
+               ? fa::launch_bwd_dq_mfma(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
                : fa::launch_bwd_dq_simt(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st);
 }
 
@@ -80,7 +80,7 @@ int fa_fwd_lse(int dtype, const void* Q, const void* K, const void* V, void* O, 
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     if (matrix_core(dtype, d))
-        return hip_status(fa::launch_fwd_d128(dtype, Q, K, V, O, L, s, scale, causal != 0,
+        return hip_status(fa::launch_fwd_mfma(dtype, Q, K, V, O, L, s, scale, causal != 0,
                                               (hipStream_t)stream));
     return hip_status(fa::launch_fwd(dtype, Q, K, V, O, L, s, scale, causal != 0,
                                      (hipStream_t)stream));
@@ -94,7 +94,7 @@ int fa_lse(int dtype, const void* Q, const void* K, float* L, int B, int H, int 
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     if (matrix_core(dtype, d))
-        return hip_status(fa::launch_lse_d128(dtype, Q, K, L, s, scale, causal != 0,
+        return hip_status(fa::launch_lse_mfma(dtype, Q, K, L, s, scale, causal != 0,
                                               (hipStream_t)stream));
     return hip_status(fa::launch_lse(dtype, Q, K, L, s, scale, causal != 0, (hipStream_t)stream));
 }

@@ -1,5 +1,7 @@
 // fwd.hip -- attention forward producing O and the logsumexp L (supporting
-// step: it feeds the backward with O and L).
+// step: it feeds the backward with O and L) on the vector ALUs: fp32 inputs,
+// and 16-bit inputs with head dims 16 and 32 (fwd_mfma.hip takes 16-bit
+// inputs with head dims 64 and 128).
 //
 // Query blocks outer, key blocks inner, online softmax per row (1point3acres
 // post "手扒了FlashAttention": running max m, denominator l and accumulator a

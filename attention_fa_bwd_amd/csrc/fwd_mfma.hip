@@ -1,5 +1,5 @@
-// fwd_mfma.hip -- attention forward on gfx950 matrix cores, bf16 and fp16, head dim 128:
-// O and the logsumexp L (supporting step: they feed the backward).
+// fwd_mfma.hip -- attention forward on gfx950 matrix cores, bf16 and fp16, head dims 64
+// and 128: O and the logsumexp L (supporting step: they feed the backward).
 //
 // Query blocks outer, key blocks inner, online softmax per query
 // (1point3acres post "手扒了FlashAttention": running max m, denominator l and
@@ -21,7 +21,8 @@
 // (accumulator layout, contraction index permuted), V^T through
 // ds_read_b64_tr_b16.  Then it turns S^T into P^T for the next phase.  All
 // waves copy parts of key block j + 2 of K and V into LDS (direct-to-LDS
-// loads); K rotates through three buffers, V through four (112 KiB).  Key rows
+// loads); K rotates through three buffers, V through four (112 KiB at
+// d = 128, 56 KiB at d = 64).  Key rows
 // at or beyond N are staged as copies of row N - 1 and masked; query rows at
 // or beyond N are not stored.
 //
@@ -40,23 +41,36 @@ using namespace mf;
 constexpr int BQ = 256;                  // queries per workgroup
 constexpr int BK = 64;                   // keys per block
 constexpr int NWAVE = 8;
-constexpr int TILE = BK * ROWB;          // 16 KiB
 constexpr int SD = 2;                    // blocks copied ahead
 constexpr int NKB = SD + 1;              // K buffers: blocks j .. j + SD
 constexpr int NVB = SD + 2;              // V buffers: blocks j - 1 .. j + SD
-constexpr int OFF_K = 0;
-constexpr int OFF_V = NKB * TILE;
-constexpr int LDS_BYTES = OFF_V + NVB * TILE;
-static_assert(LDS_BYTES == 112 * 1024, "LDS plan");
+
+// LDS plan for head dim DH
+template <int DH>
+struct Plan {
+    static constexpr int ROWB = 2 * DH;           // bytes per 16-bit row
+    static constexpr int NI = DH / 16;            // d-chunks of an S^T product's contraction
+    static constexpr int DB = DH / 32;            // 32-row blocks of d (O^T accumulators)
+    static constexpr int TILE = BK * ROWB;        // one K or V block
+    static constexpr int OFF_K = 0;
+    static constexpr int OFF_V = NKB * TILE;
+    static constexpr int LDS_BYTES = OFF_V + NVB * TILE;
+    static_assert(LDS_BYTES <= 112 * 1024, "LDS plan");
+};
 constexpr float kLazy = 8.f;             // rebase threshold, log2 units
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <typename E, bool CAUSAL, bool WITH_O>
+template <typename E, int DH, bool CAUSAL, bool WITH_O>
 __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
     e16_t* __restrict__ O, float* __restrict__ Lg, int N, int nqb, float scale) {
-    // without O only the K buffers are used (48 KiB): two workgroups fit a CU
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[WITH_O ? LDS_BYTES : OFF_V];
+    using PL = Plan<DH>;
+    constexpr int NI = PL::NI, DB = PL::DB;
+    constexpr int NSTEP = 2 * NI;  // S^T products per block (= O^T products, 4 DB)
+    static_assert(NSTEP == 4 * DB, "one O^T product per S^T product");
+    // without O only the K buffers are used (48 KiB at d = 128): two
+    // workgroups fit a CU
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[WITH_O ? PL::LDS_BYTES : PL::OFF_V];
 
     const int work = xcd_work_item(blockIdx.x, gridDim.x);
     int head = work / nqb, qblk = work % nqb;
@@ -65,7 +79,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         qblk = nqb - 1 - qblk;
     }
     const int q0 = qblk * BQ;
-    const long long hoff = (long long)head * N * D;
+    const long long hoff = (long long)head * N * DH;
     const e16_t* Kh = K + hoff;
     const e16_t* Vh = V + hoff;
 
@@ -79,39 +93,41 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
 #pragma unroll
     for (int b = 0; b < SD; ++b) {
         if (b < nblk) {
-            stage_rows<BK, NWAVE>(smem + OFF_K + b * TILE, Kh, b * BK, N, wave, l);
-            if (WITH_O) stage_rows<BK, NWAVE>(smem + OFF_V + b * TILE, Vh, b * BK, N, wave, l);
+            stage_rows<BK, NWAVE, DH>(smem + PL::OFF_K + b * PL::TILE, Kh, b * BK, N, wave, l);
+            if (WITH_O)
+                stage_rows<BK, NWAVE, DH>(smem + PL::OFF_V + b * PL::TILE, Vh, b * BK, N, wave, l);
         }
     }
     const int qc = q < N ? q : N - 1;  // clamped: finite data, row not stored
-    v16x8_t qt[8];
+    v16x8_t qt[NI];
 #pragma unroll
-    for (int dk = 0; dk < 8; ++dk)
-        qt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * D + 16 * dk + 8 * h));
+    for (int dk = 0; dk < NI; ++dk)
+        qt[dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * DH + 16 * dk + 8 * h));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     // per-lane operand offsets: S^T A operand (K row n, d-chunk i, this half);
     // V^T A operand (transposing reads of key rows 4 h + (l % 16) / 4 and + 8,
     // d-block db) -- key rows 32 + ... and 16 t + ... share their swizzle
-    int so[8], ob0[4], ob1[4];
+    int so[NI], ob0[DB], ob1[DB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) so[i] = tile_off(n, 32 * i + 16 * h);
+    for (int i = 0; i < NI; ++i) so[i] = tile_off<PL::ROWB>(n, 32 * i + 16 * h);
     {
         const int g2 = (l >> 4) & 1, x = 4 * h + ((l & 15) >> 2);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < DB; ++db) {
             const int colb = 64 * db + 32 * g2 + 8 * (l & 3);
-            ob0[db] = tile_off(x, colb);
-            ob1[db] = tile_off(x + 8, colb);
+            ob0[db] = tile_off<PL::ROWB>(x, colb);
+            ob1[db] = tile_off<PL::ROWB>(x + 8, colb);
         }
     }
-    const TileCopier<BK, NWAVE> cp(wave, l);
+    using Copier = TileCopier<BK, NWAVE, DH>;
+    const Copier cp(wave, l);
     const uint32_t lds0 = lds_addr(smem);
 
-    f32x16_t acc[4];  // O^T of d-block db: lane = query, rows 32 db + 8 (r / 4) + 4 h + r % 4
+    f32x16_t acc[DB];  // O^T of d-block db: lane = query, rows 32 db + 8 (r / 4) + 4 h + r % 4
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16_t{};
+    for (int i = 0; i < DB; ++i) acc[i] = f32x16_t{};
     v16x8_t pb[4];   // P^T of the previous block, 16-key step t = 2 mb + hh
     float mu = -1e30f, lsum = 0.f;
 
@@ -123,8 +139,8 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         // into range) to keep the loop free of branches around them
         {
             const int kn = (j + SD) * BK;
-            const uint32_t lk = lds0 + OFF_K + ((j + SD) % NKB) * TILE;
-            const uint32_t lv = lds0 + OFF_V + ((j + SD) % NVB) * TILE;
+            const uint32_t lk = lds0 + PL::OFF_K + ((j + SD) % NKB) * PL::TILE;
+            const uint32_t lv = lds0 + PL::OFF_V + ((j + SD) % NVB) * PL::TILE;
 #pragma unroll
             for (int s = 0; s < cp.SLICES; ++s) {
                 cp.copy(s, Kh, kn, N, lk);
@@ -132,16 +148,17 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
             }
         }
         const bool mf = j < nblk, pv = WITH_O && j >= 1;
-        const unsigned char* sK = smem + OFF_K + (j % NKB) * TILE;
-        const unsigned char* sV = smem + OFF_V + ((j + NVB - 1) % NVB) * TILE;
+        const unsigned char* sK = smem + PL::OFF_K + (j % NKB) * PL::TILE;
+        const unsigned char* sV = smem + PL::OFF_V + ((j + NVB - 1) % NVB) * PL::TILE;
         f32x16_t S0 = f32x16_t{}, S1 = f32x16_t{};
-        // 16 steps: S^T product i (key half i / 8, d-chunk i % 8) and O^T product
-        // i (16-key step i / 4, d-block i % 4); operands two / one steps ahead
+        // NSTEP steps: S^T product i (key half i / NI, d-chunk i % NI) and O^T
+        // product i (16-key step i / DB, d-block i % DB); operands two / one
+        // steps ahead
         v16x8_t ak[3], av[2];
-        auto kop = [&](int i) { return lds_b128(sK + so[i & 7] + 32 * ROWB * (i >> 3)); };
+        auto kop = [&](int i) { return lds_b128(sK + so[i % NI] + 32 * PL::ROWB * (i / NI)); };
         auto vop = [&](int i) {
-            const int t = i >> 2, db = i & 3;
-            return tr16_pair(sV + ob0[db] + 16 * ROWB * t, sV + ob1[db] + 16 * ROWB * t);
+            const int t = i / DB, db = i % DB;
+            return tr16_pair(sV + ob0[db] + 16 * PL::ROWB * t, sV + ob1[db] + 16 * PL::ROWB * t);
         };
         if (mf) {
             ak[0] = kop(0);
@@ -149,17 +166,17 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
         }
         if (pv) av[0] = vop(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < NSTEP; ++i) {
             if (mf) {
-                if (i + 2 < 16) ak[(i + 2) % 3] = kop(i + 2);
-                if (i < 8)
+                if (i + 2 < NSTEP) ak[(i + 2) % 3] = kop(i + 2);
+                if (i < NI)
                     S0 = E::mma(ak[i % 3], qt[i], S0);
                 else
-                    S1 = E::mma(ak[i % 3], qt[i - 8], S1);
+                    S1 = E::mma(ak[i % 3], qt[i - NI], S1);
             }
             if (pv) {
-                if (i + 1 < 16) av[(i + 1) & 1] = vop(i + 1);
-                acc[i & 3] = E::mma(av[i & 1], pb[i >> 2], acc[i & 3]);
+                if (i + 1 < NSTEP) av[(i + 1) & 1] = vop(i + 1);
+                acc[i % DB] = E::mma(av[i & 1], pb[i / DB], acc[i % DB]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -193,7 +210,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
                 lsum *= alpha;
                 if (WITH_O)
 #pragma unroll
-                    for (int db = 0; db < 4; ++db)
+                    for (int db = 0; db < DB; ++db)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
             }
@@ -221,9 +238,9 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
                                              E::pack2(p[8 * t + 6], p[8 * t + 7])));
         }
         // block j + 1's copies (issued one phase ago) must have landed; this
-        // phase's may stay in flight
+        // phase's (SLICES per tensor) may stay in flight
         if (j < jend)
-            __builtin_amdgcn_s_waitcnt(WITH_O ? kVmcnt4Lgkm0 : kVmcnt2Lgkm0);
+            __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0((WITH_O ? 2 : 1) * Copier::SLICES));
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -233,9 +250,9 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     if (q < N) {
         if (WITH_O) {
             const float inv = 1.f / ltot;
-            e16_t* orow = O + hoff + (long long)q * D;
+            e16_t* orow = O + hoff + (long long)q * DH;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const int r = 4 * a4;
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(NWAVE * 64) void fwd_mfma_kernel(
     }
 }
 
-template <typename E, bool WITH_O>
+template <typename E, int DH, bool WITH_O>
 hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O, float* L,
                            Shape s, float scale, bool causal, hipStream_t st) {
     const int nqb = (s.N + BQ - 1) / BQ;
@@ -257,30 +274,38 @@ hipError_t launch_fwd_mfma(const void* Q, const void* K, const void* V, void* O,
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((fwd_mfma_kernel<E, true, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, DH, true, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
                            nqb, scale);
     else
-        hipLaunchKernelGGL((fwd_mfma_kernel<E, false, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((fwd_mfma_kernel<E, DH, false, WITH_O>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (e16_t*)O, L, s.N,
                            nqb, scale);
     return hipGetLastError();
 }
 
+template <bool WITH_O>
+hipError_t launch_fwd_any(int dtype, const void* Q, const void* K, const void* V, void* O,
+                          float* L, Shape s, float scale, bool causal, hipStream_t st) {
+    if (s.d != 64 && s.d != 128) return hipErrorInvalidValue;
+    if (dtype == DT_F16)
+        return s.d == 64 ? launch_fwd_mfma<F16E, 64, WITH_O>(Q, K, V, O, L, s, scale, causal, st)
+                         : launch_fwd_mfma<F16E, 128, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
+    return s.d == 64 ? launch_fwd_mfma<Bf16E, 64, WITH_O>(Q, K, V, O, L, s, scale, causal, st)
+                     : launch_fwd_mfma<Bf16E, 128, WITH_O>(Q, K, V, O, L, s, scale, causal, st);
+}
+
 }  // namespace
 
-hipError_t launch_fwd_d128(int dtype, const void* Q, const void* K, const void* V, void* O,
+hipError_t launch_fwd_mfma(int dtype, const void* Q, const void* K, const void* V, void* O,
                            float* L, Shape s, float scale, bool causal, hipStream_t st) {
-    return dtype == DT_F16 ? launch_fwd_mfma<F16E, true>(Q, K, V, O, L, s, scale, causal, st)
-                           : launch_fwd_mfma<Bf16E, true>(Q, K, V, O, L, s, scale, causal, st);
+    return launch_fwd_any<true>(dtype, Q, K, V, O, L, s, scale, causal, st);
 }
 
 // L alone (no O); V is never read, K stands in for it.
-hipError_t launch_lse_d128(int dtype, const void* Q, const void* K, float* L, Shape s,
+hipError_t launch_lse_mfma(int dtype, const void* Q, const void* K, float* L, Shape s,
                            float scale, bool causal, hipStream_t st) {
-    return dtype == DT_F16
-               ? launch_fwd_mfma<F16E, false>(Q, K, K, nullptr, L, s, scale, causal, st)
-               : launch_fwd_mfma<Bf16E, false>(Q, K, K, nullptr, L, s, scale, causal, st);
+    return launch_fwd_any<false>(dtype, Q, K, K, nullptr, L, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -16,14 +16,14 @@ hipError_t launch_convert_dq(int dtype, const float* dq_accum, void* dQ, Shape s
 hipError_t launch_fwd(int dtype, const void* Q, const void* K, const void* V, void* O,
                       float* L, Shape s, float scale, bool causal, hipStream_t st);
 
-// Matrix-core forward, bf16 or fp16 (dtype), head dim 128.
-hipError_t launch_fwd_d128(int dtype, const void* Q, const void* K, const void* V, void* O,
+// Matrix-core forward, bf16 or fp16 (dtype), head dim 64 or 128.
+hipError_t launch_fwd_mfma(int dtype, const void* Q, const void* K, const void* V, void* O,
                            float* L, Shape s, float scale, bool causal, hipStream_t st);
 
 // L alone, by the same two forward kernels without V and O.
 hipError_t launch_lse(int dtype, const void* Q, const void* K, float* L, Shape s, float scale,
                       bool causal, hipStream_t st);
-hipError_t launch_lse_d128(int dtype, const void* Q, const void* K, float* L, Shape s,
+hipError_t launch_lse_mfma(int dtype, const void* Q, const void* K, float* L, Shape s,
                            float scale, bool causal, hipStream_t st);
 
 // Vector-ALU backward (fp32 FMA), every dtype and head dim: key-outer dK/dV
@@ -35,12 +35,12 @@ hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const voi
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);
 
-// Matrix-core backward, bf16 or fp16 (dtype), head dim 128: key-outer dK/dV
-// pass and query-outer dQ pass (dq_accum rows written once, unscaled).
-hipError_t launch_bwd_dkdv_d128(int dtype, const void* Q, const void* K, const void* V,
+// Matrix-core backward, bf16 or fp16 (dtype), head dim 64 or 128: key-outer
+// dK/dV pass and query-outer dQ pass (dq_accum rows written once, unscaled).
+hipError_t launch_bwd_dkdv_mfma(int dtype, const void* Q, const void* K, const void* V,
                                 const void* dO, const float* L, const float* D, void* dK,
                                 void* dV, Shape s, float scale, bool causal, hipStream_t st);
-hipError_t launch_bwd_dq_d128(int dtype, const void* Q, const void* K, const void* V,
+hipError_t launch_bwd_dq_mfma(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);
 

@@ -1,5 +1,6 @@
-// mfma_common.hpp -- CDNA4 (gfx950) matrix-core helpers shared by the two
-// backward kernels (key-outer dK/dV, query-outer dQ).
+// mfma_common.hpp -- CDNA4 (gfx950) matrix-core helpers shared by the
+// matrix-core kernels (key-outer dK/dV pass, query-outer dQ pass, forward),
+// head dims 64 and 128.
 //
 // Operand layouts of v_mfma_f32_32x32x16_bf16 and _f16 (the same; checked on
 // the hardware):
@@ -40,13 +41,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // s_waitcnt operand that waits for LDS (and scalar) traffic only: vmcnt and
 // expcnt at their maxima, lgkmcnt 0.
 constexpr int kLgkmOnly = 0xC07F;
-// s_waitcnt operand: at most 8 vector-memory operations outstanding, LDS and
-// scalar traffic drained (vmcnt 8, expcnt 7, lgkmcnt 0).
-constexpr int kVmcnt8Lgkm0 = 0x0078;
-constexpr int kVmcnt4Lgkm0 = 0x0074;
-constexpr int kVmcnt2Lgkm0 = 0x0072;
-constexpr int D = 128;       // head dim of the matrix-core kernels
-constexpr int ROWB = D * 2;  // bytes per 16-bit row of Q, K, V, dO
+// s_waitcnt operand: at most n (< 16) vector-memory operations outstanding,
+// LDS and scalar traffic drained (vmcnt n, expcnt 7, lgkmcnt 0).
+constexpr int vmcnt_lgkm0(int n) { return 0x0070 | n; }
 
 __device__ __forceinline__ f32x16_t mfma(const v16x8_t& a, const v16x8_t& b, const f32x16_t& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -85,18 +82,30 @@ __device__ __forceinline__ v16x8_t tr16_pair(const unsigned char* p0, const unsi
     return __builtin_bit_cast(v16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// 16-byte chunk swizzle of a 256-byte row (16 chunks), XORed into the chunk
-// index.  LDS has 64 banks of 4 bytes (256 bytes per cycle).  The row-wise
-// operand reads (ds_read_b128: 16 lanes, 16 consecutive rows, one logical
-// chunk) need the 16 rows on 16 distinct chunks; the transposing reads
-// (4 consecutive rows x one 64-byte group of 4 chunks per 32 lanes) need the 4
-// rows on 4 distinct 64-byte groups.  Bits [3:2] of the XOR therefore come from
-// row bits [1:0] and bits [1:0] from row bits [3:2].
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// 16-byte chunk swizzle of an LDS tile row of ROWB bytes (the head dim DH of
+// the matrix-core kernels is 64 or 128: rows of 128 or 256 bytes, 8 or 16
+// chunks), XORed into the chunk index.  LDS has 64 banks of 4 bytes (256
+// bytes per cycle).  The row-wise operand reads (ds_read_b128: 16 lanes, 16
+// consecutive rows, one logical chunk) need the 16 rows on 16 distinct
+// 16-byte bank slots; the transposing reads (4 consecutive rows x one 64-byte
+// block per 32 lanes) need the 4 rows on 4 distinct 64-byte bank groups.
+//   256-byte rows: bits [3:2] of the XOR from row bits [1:0], bits [1:0] from
+//                  row bits [3:2].
+//   128-byte rows: a row pair fills the 256 bank bytes, so row bit 0 already
+//                  separates the halves; bit 2 of the XOR from row bit 1,
+//                  bits [1:0] from row bits [3:2].
+// Both depend on the row modulo 16 only.
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+    static_assert(ROWB == 256 || ROWB == 128, "rows of 64 or 128 16-bit elements");
+    return ROWB == 256 ? (((row & 3) << 2) | ((row >> 2) & 3))
+                       : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
+}
 
-// Byte offset of (row, byte column) in a swizzled 256-byte-row tile.
+// Byte offset of (row, byte column) in a swizzled tile of ROWB-byte rows.
+template <int ROWB>
 __device__ __forceinline__ int tile_off(int row, int colb) {
-    return row * ROWB + ((((colb >> 4) ^ swz(row)) << 4) | (colb & 15));
+    return row * ROWB + ((((colb >> 4) ^ swz<ROWB>(row)) << 4) | (colb & 15));
 }
 
 // One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes at src land at
@@ -119,15 +128,16 @@ __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
-// Copy rows [r0, r0 + nrows) of a [N, 128] 16-bit matrix into a swizzled LDS
+// Copy rows [r0, r0 + NROWS) of a [N, DH] 16-bit matrix into a swizzled LDS
 // tile with direct-to-LDS loads: each wave moves 1 KiB (64 lanes x 16 bytes)
 // per instruction, lane i landing at byte 16 i of the wave's slice, so lane i
 // fetches the logical chunk that the swizzle places there.  Rows at or beyond
 // N are clamped to row N - 1 (finite data; callers make them contribute 0).
 // UNTRACKED: issue through lds_copy16 (the caller waits before use).
-template <int NROWS, int NWAVES, bool UNTRACKED = false>
+template <int NROWS, int NWAVES, int DH, bool UNTRACKED = false>
 __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const e16_t* src, int r0,
                                            int N, int wave, int lane) {
+    constexpr int ROWB = 2 * DH;
     constexpr int BYTES = NROWS * ROWB;
     constexpr int PER_WAVE = BYTES / NWAVES;
     static_assert(PER_WAVE % 1024 == 0, "tile must split into 1 KiB slices per wave");
@@ -135,10 +145,10 @@ __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const e16_t*
     for (int j = 0; j < PER_WAVE / 1024; ++j) {
         const int p = wave * PER_WAVE + j * 1024 + lane * 16;
         const int row = p / ROWB;
-        const int chunk = ((p % ROWB) >> 4) ^ swz(row);
+        const int chunk = ((p % ROWB) >> 4) ^ swz<ROWB>(row);
         int g = r0 + row;
         g = g < N ? g : N - 1;
-        const e16_t* gp = src + (long long)g * D + chunk * 8;
+        const e16_t* gp = src + (long long)g * DH + chunk * 8;
         unsigned char* lp = lds_tile + wave * PER_WAVE + j * 1024;
         if (UNTRACKED)
             lds_copy16(gp, __builtin_amdgcn_readfirstlane(
@@ -159,15 +169,16 @@ __device__ __forceinline__ void lds_copy16_sbase(const void* base, uint32_t voff
 }
 #pragma clang diagnostic pop
 
-// Copies NROWS-row tiles of [N, 128] 16-bit matrices into swizzled LDS tiles
+// Copies NROWS-row tiles of [N, DH] 16-bit matrices into swizzled LDS tiles
 // with NWAVES waves, one 1 KiB slice (one direct-to-LDS copy) at a time, so
 // that the copies of a tile can be spread over the work of a loop iteration.
 // The per-lane byte offsets of the slices are computed once; a full tile then
 // needs two vector operations per copy.  Rows at or beyond N (a ragged last
 // tile) are clamped to row N - 1.  Callers wait (vmcnt(0)) and synchronise
 // before any wave reads the tile.
-template <int NROWS, int NWAVES>
+template <int NROWS, int NWAVES, int DH>
 struct TileCopier {
+    static constexpr int ROWB = 2 * DH;
     static constexpr int PER_WAVE = NROWS * ROWB / NWAVES;
     static constexpr int SLICES = PER_WAVE / 1024;
     static_assert(PER_WAVE % 1024 == 0, "tile must split into 1 KiB slices per wave");
@@ -181,7 +192,7 @@ struct TileCopier {
         for (int j = 0; j < SLICES; ++j) {
             const int p = wave * PER_WAVE + j * 1024 + lane * 16;
             const int row = p / ROWB;
-            const int chunk = ((p % ROWB) >> 4) ^ swz(row);
+            const int chunk = ((p % ROWB) >> 4) ^ swz<ROWB>(row);
             rowj[j] = row;
             voff[j] = (uint32_t)(row * ROWB + chunk * 16);
         }
@@ -196,7 +207,7 @@ struct TileCopier {
         const int rb = r0 < N ? r0 : N - 1;
         const int lim = N - 1 - rb;
         const int row = rowj[j] < lim ? rowj[j] : lim;
-        lds_copy16_sbase(src + (long long)rb * D,
+        lds_copy16_sbase(src + (long long)rb * DH,
                          (uint32_t)(row * ROWB) + (voff[j] & (ROWB - 1)),
                          lds_tile + lds_wave + j * 1024);
     }

@@ -74,7 +74,7 @@ typedef enum {
  * (1point3acres post "手扒了FlashAttention", the online-softmax recurrence and
  * the logsumexp; FA2 chapter 16 sec 16.4).  Supporting step of the backward:
  * it provides O and L for benchmarking and end-to-end checks.  bf16 and fp16
- * with d = 128 run on the matrix cores and rebase lazily (only when a block's
+ * with d = 64 or 128 run on the matrix cores and rebase lazily (only when a block's
  * maximum exceeds the running one by more than a factor 2^8, which leaves
  * O and L unchanged in exact arithmetic); other cases run a vector-ALU kernel.
  *   in : Q, K, V [B,H,N,d] dtype
@@ -120,7 +120,8 @@ int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D,
  *   One contract for every dtype and head dim: dq_accum is overwritten (its
  *   prior contents are never read), no atomics are used, and dq_accum, dK
  *   and dV are bitwise reproducible from call to call.  bf16 and fp16 with
- *   d = 128 run on the matrix cores; the other pairs on the vector ALUs.
+ *   d = 64 or 128 run on the matrix cores; fp32, and 16-bit d = 16 or 32, on
+ *   the vector ALUs.
  *   in : Q, K, V, dO [B,H,N,d] dtype; L, D [B,H,N] fp32
  *   out: dq_accum [B,H,N,d] fp32 = sum_j dS_ij K_j (unscaled);
  *        dK, dV [B,H,N,d] dtype

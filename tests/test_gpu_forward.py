@@ -1,8 +1,8 @@
 """GPU parity of the forward (fa_fwd_lse) and of L alone (fa_lse): O and L
 against the oracle's plain definition, element by element.
 
-bf16 and fp16 with d = 128 run the matrix-core kernel (lazy rebase of the running
-maximum); the other cases run the vector-ALU kernel.  Tolerances: O within the
+bf16 and fp16 with d = 64 or 128 run the matrix-core kernel (lazy rebase of the
+running maximum); the other cases run the vector-ALU kernel.  Tolerances: O within the
 element type's bar (max |err| / max |ref|), L (natural log, fp32) within 1e-4
 absolute -- S comes from exact 16-bit products accumulated in fp32, so L is
 accurate to a few fp32 ulps of the scores."""
@@ -35,32 +35,34 @@ def _check(inp, causal, what, l_tol=1e-4):
     assert el <= l_tol, f"{what}: L abs err {el:.3e}"
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 200, 255, 256, 257, 600])
-def test_d128_shapes(N, causal, dtype):
+def test_matrix_core_shapes(N, causal, dtype, d):
     """Matrix-core forward: tiny, ragged and multi-block N (the workgroup holds
     256 queries, key blocks are 64 rows)."""
-    gu.note(f"case fwd {dtype} d=128 N={N} causal={causal}")
-    inp = si.draw_custom(2, 2, N, 128, dtype, seed=300 + N)
-    _check(inp, causal, f"N={N}")
+    gu.note(f"case fwd {dtype} d={d} N={N} causal={causal}")
+    inp = si.draw_custom(2, 2, N, d, dtype, seed=300 + N + d)
+    _check(inp, causal, f"N={N} d={d}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d,dtype", [(16, "fp32"), (64, "bf16"), (64, "fp16"), (128, "fp32")])
+@pytest.mark.parametrize("d,dtype", [(16, "fp32"), (32, "bf16"), (16, "fp16"), (128, "fp32")])
 def test_vector_alu_forward(d, dtype, causal):
     gu.note(f"case fwd {dtype} d={d} causal={causal}")
     inp = si.draw_custom(1, 2, 133, d, dtype, seed=400 + d)
     _check(inp, causal, f"{dtype} d={d}", l_tol=1e-6 if dtype == "fp32" else 1e-4)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("q_mult", [4.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_bf16_d128_large_scores(q_mult, causal):
+def test_bf16_large_scores(q_mult, causal, d):
     """Peaky softmax: row maxima of tens to hundreds in exp2 units, so the
     running maximum moves by more than the lazy threshold many times."""
-    gu.note(f"case fwd large scores q x{q_mult} causal={causal}")
-    inp = si.draw_custom(1, 2, 700, 128, "bf16", seed=500 + int(q_mult), q_mult=q_mult)
+    gu.note(f"case fwd large scores d={d} q x{q_mult} causal={causal}")
+    inp = si.draw_custom(1, 2, 700, d, "bf16", seed=500 + int(q_mult), q_mult=q_mult)
     _check(inp, causal, f"q x{q_mult}", l_tol=1e-3)
 
 
@@ -78,7 +80,7 @@ def test_bf16_d128_growing_max():
     _check(inp, False, "growing max", l_tol=1e-3)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 32),
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp16", 128), ("bf16", 64), ("fp16", 64), ("fp16", 32),
                                      ("fp32", 16), ("fp32", 128)])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 63, 257, 600])

@@ -129,34 +129,53 @@ def test_edge_shapes(N, d, dtype, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [300, 520])
-def test_multi_block_ragged_d128(N, dtype, causal):
-    """Head dim 128, 16-bit: more than one 256-query block of the dQ pass and
+def test_multi_block_ragged(N, d, dtype, causal):
+    """Matrix-core head dims: more than one 256-query block of the dQ pass and
     more than one 128-key block of the dK/dV pass, the last of each ragged
     (N = 300: 44 rows in the second query block, so three of its four score
     waves own only rows past N; N = 520: 8 rows in the third).  Full tensors
     against the oracle, end to end and with the oracle's O and L."""
-    gu.note(f"case multi-block ragged N={N} d=128 {dtype} causal={causal}")
-    inp = si.draw_custom(2, 2, N, 128, dtype, seed=900 + N)
+    gu.note(f"case multi-block ragged N={N} d={d} {dtype} causal={causal}")
+    inp = si.draw_custom(2, 2, N, d, dtype, seed=900 + N + d)
     out = gu.run_gpu(inp, causal)
     errs = gu.compare_full(inp, causal, out)
-    _assert_grads(errs, gu.TOL[dtype], f"N={N} {dtype} end to end")
+    _assert_grads(errs, gu.TOL[dtype], f"N={N} d={d} {dtype} end to end")
     O, L = oracle.attn_fwd(inp.Q, inp.K, inp.V, inp.wl.scale, causal)
     Os = _stored(O, dtype)
     out = gu.run_gpu(inp, causal, O=Os, L=L)
     rq, rk, rv = oracle.flash_bwd_tiled(inp.Q, inp.K, inp.V, Os, inp.dO, L, inp.wl.scale, causal, 16, 12)
     errs = {n: gu.rel_err(gu.to_f64(out[n]), r) for n, r in (("dq", rq), ("dk", rk), ("dv", rv))}
-    _assert_grads(errs, gu.TOL[dtype], f"N={N} {dtype} isolated")
+    _assert_grads(errs, gu.TOL[dtype], f"N={N} d={d} {dtype} isolated")
     assert not gu.invariants(inp, causal, out)["nan"]
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_xcd_order_and_head_pairs(d, causal):
+    """B=1 H=16 N=1024: every pass has a work-item count divisible by the 8 XCDs
+    (dK/dV 8 key blocks x 16 heads, dQ and forward 4 query blocks x 16 heads),
+    so the XCD-contiguous order is on, and under the causal mask each XCD's
+    share holds whole head pairs, so the heavy-first pair interleave is on
+    too.  Whole tensors against the oracle."""
+    gu.note(f"case xcd order / head pairs d={d} causal={causal}")
+    inp = si.draw_custom(1, 16, 1024, d, "bf16", seed=1200 + d)
+    out = gu.run_gpu(inp, causal)
+    errs = gu.compare_full(inp, causal, out)
+    gu.note(f"  errs {errs}")
+    _assert_grads(errs, gu.TOL["bf16"], f"H=16 N=1024 d={d}")
+    assert errs["o"] <= gu.TOL["bf16"] and errs["L"] <= 1e-3
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("q_mult", [4.0, 8.0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_large_scores(q_mult, causal, dtype):
+def test_large_scores(q_mult, causal, dtype, d):
     """Peaky softmax: Q scaled up so row maxima are large and land anywhere."""
-    gu.note(f"case large scores q x{q_mult} causal={causal} {dtype}")
-    inp = si.draw_custom(2, 2, 300, 128, dtype, seed=17, q_mult=q_mult)
+    gu.note(f"case large scores d={d} q x{q_mult} causal={causal} {dtype}")
+    inp = si.draw_custom(2, 2, 300, d, dtype, seed=17, q_mult=q_mult)
     out = gu.run_gpu(inp, causal)
     errs = gu.compare_full(inp, causal, out)
     gu.note(f"  errs {errs}")
