@@ -117,6 +117,36 @@ def compare_sampled(inp: si.Inputs, causal: bool, out: dict, heads, nrows: int =
     return errs
 
 
+def compare_heads(inp: si.Inputs, causal: bool, out: dict, heads, log=None) -> dict:
+    """Every element of dQ, dK, dV and O of whole (b, h) heads against the
+    oracle's plain definitions (oracle.attn_bwd and attn_fwd on that head
+    alone), and L as the largest absolute difference.  Returns the error
+    measure over all compared elements per tensor, and per head."""
+    scale = inp.wl.scale
+    acc = {n: [0.0, 0.0] for n in ("dq", "dk", "dv", "o")}   # max |err|, max |ref|
+    per_head = {}
+    lerr = 0.0
+    for (b, h) in heads:
+        sl = lambda x: np.ascontiguousarray(x[b:b + 1, h:h + 1], dtype=np.float64)
+        dQ, dK, dV, _ = oracle.attn_bwd(sl(inp.Q), sl(inp.K), sl(inp.V), sl(inp.dO), scale, causal)
+        O, L = oracle.attn_fwd(sl(inp.Q), sl(inp.K), sl(inp.V), scale, causal)
+        lerr = max(lerr, float(np.abs(to_f64(out["L"][b:b + 1, h:h + 1]) - L).max()))
+        errs = {}
+        for name, ref in (("dq", dQ), ("dk", dK), ("dv", dV), ("o", O)):
+            g = to_f64(out[name][b:b + 1, h:h + 1])
+            num, den = float(np.abs(g - ref).max()), float(np.abs(ref).max())
+            acc[name][0] = max(acc[name][0], num)
+            acc[name][1] = max(acc[name][1], den)
+            errs[name] = num / den if den > 0 else num
+        per_head[(b, h)] = errs
+        if log:
+            log(f"  head ({b},{h}): " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    res = {n: (a[0] / a[1] if a[1] > 0 else a[0]) for n, a in acc.items()}
+    res["L"] = lerr
+    res["per_head"] = per_head
+    return res
+
+
 def invariants(inp: si.Inputs, causal: bool, out: dict) -> dict:
     """Properties exact in real arithmetic, checked on whole GPU outputs:
     sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, and (causal) dQ_0 = 0."""
@@ -139,4 +169,4 @@ def flops_note(inp: si.Inputs, causal: bool) -> float:
 
 
 __all__ = ["TOL", "note", "upload", "to_f64", "rel_err", "run_gpu", "compare_full",
-           "compare_sampled", "invariants", "sample_rows", "flops_note", "math"]
+           "compare_sampled", "compare_heads", "invariants", "sample_rows", "flops_note", "math"]
