@@ -15,14 +15,15 @@ import torch
 __all__ = [
     "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "FAError", "lib_path", "load",
     "fa_fwd_lse", "fa_lse", "fa_bwd_preprocess", "fa_bwd", "fa_bwd_dkdv", "fa_bwd_dq",
-    "fa_bwd_convert_dq", "fa_strerror",
+    "fa_bwd_convert_dq", "fa_bwd_noalloc", "fa_strerror",
     "forward", "lse", "backward",
 ]
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_F16 = 2
-FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP = 0, 1, 2, 3
+FA_OK, FA_EINVAL, FA_EUNSUPPORTED, FA_EHIP, FA_ESCRATCH = 0, 1, 2, 3, 4
+FA_NOALLOC_MAX_ROWS = 1 << 22   # B * H * N rows that fa_bwd_noalloc's scratch holds
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfa_bwd.so")
@@ -38,6 +39,7 @@ _SIGS = {
     "fa_bwd_dkdv": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_dq": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_bwd_convert_dq": [_i, _vp, _vp, _i, _i, _i, _i, _f, _vp],
+    "fa_bwd_noalloc": [_i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp],
     "fa_last_hip_error": [],
 }
 
@@ -193,6 +195,19 @@ def fa_bwd_convert_dq(dq_accum, dq, scale: float, stream=None) -> None:
     ptrs = _ptrs(dq, (dq_accum, torch.float32, s4), (dq, dq.dtype, s4))
     rc = load().fa_bwd_convert_dq(_dtype_code(dq), *ptrs, *s4, float(scale), _stream(stream))
     _check("fa_bwd_convert_dq", rc)
+
+
+def fa_bwd_noalloc(q, k, v, o, do, L, dq, dk, dv, scale: float, causal: bool,
+                   stream=None) -> None:
+    """The whole backward with no device allocation (D in the library's static
+    scratch, dQ written scaled by the dQ pass)."""
+    s4, s3 = _sizes(q)
+    e = q.dtype
+    ptrs = _ptrs(q, (q, e, s4), (k, e, s4), (v, e, s4), (o, e, s4), (do, e, s4),
+                 (L, torch.float32, s3), (dq, e, s4), (dk, e, s4), (dv, e, s4))
+    rc = load().fa_bwd_noalloc(_dtype_code(q), *ptrs, *s4, float(scale), int(bool(causal)),
+                               _stream(stream))
+    _check("fa_bwd_noalloc", rc)
 
 
 def forward(q, k, v, scale: float, causal: bool, stream=None):

@@ -1,8 +1,17 @@
 // api.hip -- the extern "C" entry points declared in include/fa_bwd.h:
-// argument validation, then one launcher per call.  No allocation, no global
-// mutable state other than the calling thread's last HIP error code.
+// argument validation, then one launcher per call.  No allocation; the only
+// global mutable state is the calling thread's last HIP error code and, for
+// fa_bwd_noalloc, the per-device address of its static scratch array.
+#include <mutex>
+
 #include "../../include/fa_bwd.h"
 #include "launch.hpp"
+
+// D (one fp32 per row) of fa_bwd_noalloc: a static device array of the
+// library, one copy per GPU, held until the process ends.  In host code this
+// name stands for the host-side shadow of the array, not a device address:
+// kernels get the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
 
 namespace {
 
@@ -66,6 +75,37 @@ hipError_t launch_dq(int dtype, const void* Q, const void* K, const void* V, con
     return matrix_core(dtype, s.d)
                ? fa::launch_bwd_dq_mfma(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
                : fa::launch_bwd_dq_simt(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st);
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_for_current_device(float** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+// The dQ pass writing the scaled dQ in the element type (no dq_accum).
+hipError_t launch_dq_direct(int dtype, const void* Q, const void* K, const void* V,
+                            const void* dO, const float* L, const float* D, void* dQ,
+                            fa::Shape s, float scale, bool causal, hipStream_t st) {
+    return matrix_core(dtype, s.d)
+               ? fa::launch_bwd_dq_mfma_direct(dtype, Q, K, V, dO, L, D, dQ, s, scale, causal, st)
+               : fa::launch_bwd_dq_simt_direct(dtype, Q, K, V, dO, L, D, dQ, s, scale, causal, st);
 }
 
 }  // namespace
@@ -154,12 +194,35 @@ int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ, int B, int H, 
                                             (hipStream_t)stream));
 }
 
+int fa_bwd_noalloc(int dtype, const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* L, void* dQ, void* dK, void* dV, int B, int H,
+                   int N, int d, float scale, int causal, void* stream) {
+    int rc = check(dtype, B, H, N, d, {Q, K, V, O, dO, L, dQ, dK, dV});
+    if (rc != FA_OK) return rc;
+    if (!scale_ok(scale)) return FA_EINVAL;
+    if ((long long)B * H * N > FA_NOALLOC_MAX_ROWS) return FA_ESCRATCH;
+    if ((rc = device_ready()) != FA_OK) return rc;
+    float* Dbuf = nullptr;
+    if ((rc = hip_status(scratch_for_current_device(&Dbuf))) != FA_OK) return rc;
+    const fa::Shape s{B, H, N, d};
+    const hipStream_t st = (hipStream_t)stream;
+    // D into the scratch array, then the dQ pass (dQ scaled and cast in its
+    // epilogue) and the dK/dV pass, in order on the caller's stream
+    if ((rc = hip_status(fa::launch_preprocess(dtype, O, dO, Dbuf, s, st))) != FA_OK) return rc;
+    rc = hip_status(launch_dq_direct(dtype, Q, K, V, dO, L, Dbuf, dQ, s, scale, causal != 0, st));
+    if (rc != FA_OK) return rc;
+    return hip_status(
+        launch_dkdv(dtype, Q, K, V, dO, L, Dbuf, dK, dV, s, scale, causal != 0, st));
+}
+
 const char* fa_strerror(int status) {
     switch (status) {
         case FA_OK: return "success";
         case FA_EINVAL: return "invalid argument (null or misaligned pointer, bad size or dtype)";
         case FA_EUNSUPPORTED: return "unsupported head dimension (supported: 16, 32, 64, 128)";
         case FA_EHIP: return "HIP runtime error (see fa_last_hip_error)";
+        case FA_ESCRATCH:
+            return "problem too large for fa_bwd_noalloc (B * H * N above FA_NOALLOC_MAX_ROWS)";
     }
     return "unknown status";
 }

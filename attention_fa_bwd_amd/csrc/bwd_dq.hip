@@ -257,11 +257,14 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
     }
 }
 
-template <typename E, int DH, bool CAUSAL>
+// DIRECT: instead of the unscaled fp32 dq_accum, write dQ = scale * acc in the
+// element type (round to nearest even), exactly what the convert step makes of
+// dq_accum; out is then the dQ tensor.
+template <typename E, int DH, bool CAUSAL, bool DIRECT>
 __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
     const e16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
-    float* __restrict__ dqa, int N, int nqb, float scale) {
+    void* __restrict__ dq_out, int N, int nqb, float scale) {
     using PL = Plan<DH>;
     constexpr int NI = PL::NI;
     constexpr int QGW = DH / 32;  // query groups per gradient wave
@@ -413,44 +416,74 @@ __global__ __launch_bounds__(NWAVE * 64) void bwd_dq_kernel(
 
     // epilogue: acc[qg][dt] holds dQ for queries q0 + 32 (qg0 + qg) + 8 (r / 4) +
     // 4 h + r % 4, column 32 (dt0 + dt) + n
-    float* out = dqa + hoff;
+    if constexpr (DIRECT) {
+        e16_t* out = reinterpret_cast<e16_t*>(dq_out) + hoff;
 #pragma unroll
-    for (int qg = 0; qg < QGW; ++qg)
+        for (int qg = 0; qg < QGW; ++qg)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qq = q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
-            float* orow = out + (long long)qq * DH + 32 * dt0 + n;
-            if (qq < N)
+            for (int r = 0; r < 16; ++r) {
+                const int qq = q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
+                e16_t* orow = out + (long long)qq * DH + 32 * dt0 + n;
+                if (qq < N)
 #pragma unroll
-                for (int dt = 0; dt < 2; ++dt) orow[32 * dt] = acc[qg][dt][r];
-        }
+                    for (int dt = 0; dt < 2; ++dt) {
+                        // the fp32 product first, as the convert step forms
+                        // it (not fused into one mixed-precision rounding)
+                        float x = acc[qg][dt][r] * scale;
+                        pin(x);
+                        orow[32 * dt] = (e16_t)(E::pack2(x, 0.f) & 0xffffu);
+                    }
+            }
+    } else {
+        float* out = reinterpret_cast<float*>(dq_out) + hoff;
+#pragma unroll
+        for (int qg = 0; qg < QGW; ++qg)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qq = q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
+                float* orow = out + (long long)qq * DH + 32 * dt0 + n;
+                if (qq < N)
+#pragma unroll
+                    for (int dt = 0; dt < 2; ++dt) orow[32 * dt] = acc[qg][dt][r];
+            }
+    }
 }
 
-template <typename E, int DH>
+template <typename E, int DH, bool DIRECT>
 hipError_t launch_dq(const void* Q, const void* K, const void* V, const void* dO, const float* L,
-                     const float* Dv, float* dqa, Shape s, float scale, bool causal,
+                     const float* Dv, void* out, Shape s, float scale, bool causal,
                      hipStream_t st) {
     const int nqb = (s.N + BQ - 1) / BQ;
     const long long nwork = (long long)nqb * s.H * s.B;
     if (nwork > 0x7fffffffLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)nwork);
     if (causal)
-        hipLaunchKernelGGL((bwd_dq_kernel<E, DH, true>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((bwd_dq_kernel<E, DH, true, DIRECT>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO, L,
-                           Dv, dqa, s.N, nqb, scale);
+                           Dv, out, s.N, nqb, scale);
     else
-        hipLaunchKernelGGL((bwd_dq_kernel<E, DH, false>), grid, dim3(NWAVE * 64), 0, st,
+        hipLaunchKernelGGL((bwd_dq_kernel<E, DH, false, DIRECT>), grid, dim3(NWAVE * 64), 0, st,
                            (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO, L,
-                           Dv, dqa, s.N, nqb, scale);
+                           Dv, out, s.N, nqb, scale);
     return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, bool DIRECT>
 hipError_t launch_dq_e(const void* Q, const void* K, const void* V, const void* dO,
-                       const float* L, const float* Dv, float* dqa, Shape s, float scale,
+                       const float* L, const float* Dv, void* out, Shape s, float scale,
                        bool causal, hipStream_t st) {
-    return s.d == 64 ? launch_dq<E, 64>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st)
-                     : launch_dq<E, 128>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
+    return s.d == 64 ? launch_dq<E, 64, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st)
+                     : launch_dq<E, 128, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
+}
+
+template <bool DIRECT>
+hipError_t launch_dq_any(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+                         const float* L, const float* Dv, void* out, Shape s, float scale,
+                         bool causal, hipStream_t st) {
+    if (s.d != 64 && s.d != 128) return hipErrorInvalidValue;
+    return dtype == DT_F16
+               ? launch_dq_e<F16E, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st)
+               : launch_dq_e<Bf16E, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
 }
 
 }  // namespace
@@ -458,9 +491,13 @@ hipError_t launch_dq_e(const void* Q, const void* K, const void* V, const void* 
 hipError_t launch_bwd_dq_mfma(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* Dv, float* dqa,
                               Shape s, float scale, bool causal, hipStream_t st) {
-    if (s.d != 64 && s.d != 128) return hipErrorInvalidValue;
-    return dtype == DT_F16 ? launch_dq_e<F16E>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st)
-                           : launch_dq_e<Bf16E>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
+    return launch_dq_any<false>(dtype, Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
+}
+
+hipError_t launch_bwd_dq_mfma_direct(int dtype, const void* Q, const void* K, const void* V,
+                                     const void* dO, const float* L, const float* Dv, void* dQ,
+                                     Shape s, float scale, bool causal, hipStream_t st) {
+    return launch_dq_any<true>(dtype, Q, K, V, dO, L, Dv, dQ, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -146,11 +146,14 @@ __global__ __launch_bounds__(256) void simt_dkdv_kernel(
     }
 }
 
-template <typename T, int D, int BC, int BR, bool CAUSAL>
+// DIRECT: instead of the unscaled fp32 dq_accum, write dQ = scale * acc in the
+// element type (round to nearest even), exactly what the convert step makes of
+// dq_accum; out is then the dQ tensor.
+template <typename T, int D, int BC, int BR, bool CAUSAL, bool DIRECT>
 __global__ __launch_bounds__(256) void simt_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-    float* __restrict__ dqa, int N, float scale) {
+    void* __restrict__ out, int N, float scale) {
     using W = SimtSplit<D, BC, BR>;
     constexpr int DQ_OUT = BR * D / W::NT;  // dQ accumulators per lane
     static_assert(DQ_OUT >= 1 && DQ_OUT * W::NT == BR * D, "tile too small");
@@ -199,7 +202,15 @@ __global__ __launch_bounds__(256) void simt_dq_kernel(
 #pragma unroll
     for (int u = 0; u < DQ_OUT; ++u) {
         const int i = q0 + rbase + W::CSTEP * u;
-        if (i < N) dqa[hoff + (long long)i * D + kcol] = acc[u];
+        if (i >= N) continue;
+        if constexpr (DIRECT) {
+            // the fp32 product first, as the convert step forms it (not fused
+            // into one mixed-precision rounding)
+            float x = acc[u] * scale;
+            asm volatile("" : "+v"(x));
+            reinterpret_cast<T*>(out)[hoff + (long long)i * D + kcol] = from_f32<T>(x);
+        } else
+            reinterpret_cast<float*>(out)[hoff + (long long)i * D + kcol] = acc[u];
     }
 }
 
@@ -226,18 +237,18 @@ hipError_t dkdv_t(const void* Q, const void* K, const void* V, const void* dO, c
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool DIRECT>
 hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, const float* L,
-                const float* Dv, float* dqa, Shape s, float scale, bool causal, hipStream_t st) {
+                const float* Dv, void* out, Shape s, float scale, bool causal, hipStream_t st) {
     constexpr int BT = simt_tile<D>();
     dim3 grid((s.N + BT - 1) / BT, s.H, s.B);
     if (causal)
-        hipLaunchKernelGGL((simt_dq_kernel<T, D, BT, BT, true>), grid, dim3(256), 0, st,
-                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, dqa, s.N,
+        hipLaunchKernelGGL((simt_dq_kernel<T, D, BT, BT, true, DIRECT>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, out, s.N,
                            scale);
     else
-        hipLaunchKernelGGL((simt_dq_kernel<T, D, BT, BT, false>), grid, dim3(256), 0, st,
-                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, dqa, s.N,
+        hipLaunchKernelGGL((simt_dq_kernel<T, D, BT, BT, false, DIRECT>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, out, s.N,
                            scale);
     return hipGetLastError();
 }
@@ -255,16 +266,25 @@ hipError_t dkdv_d(const void* Q, const void* K, const void* V, const void* dO, c
     return hipErrorInvalidValue;
 }
 
-template <typename T>
+template <typename T, bool DIRECT>
 hipError_t dq_d(const void* Q, const void* K, const void* V, const void* dO, const float* L,
-                const float* Dv, float* dqa, Shape s, float scale, bool causal, hipStream_t st) {
+                const float* Dv, void* out, Shape s, float scale, bool causal, hipStream_t st) {
     switch (s.d) {
-        case 16: return dq_t<T, 16>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
-        case 32: return dq_t<T, 32>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
-        case 64: return dq_t<T, 64>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
-        case 128: return dq_t<T, 128>(Q, K, V, dO, L, Dv, dqa, s, scale, causal, st);
+        case 16: return dq_t<T, 16, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
+        case 32: return dq_t<T, 32, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
+        case 64: return dq_t<T, 64, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
+        case 128: return dq_t<T, 128, DIRECT>(Q, K, V, dO, L, Dv, out, s, scale, causal, st);
     }
     return hipErrorInvalidValue;
+}
+
+template <bool DIRECT>
+hipError_t dq_any(int dtype, const void* Q, const void* K, const void* V, const void* dO,
+                  const float* L, const float* D, void* out, Shape s, float scale, bool causal,
+                  hipStream_t st) {
+    return dtype == DT_BF16  ? dq_d<bf16_t, DIRECT>(Q, K, V, dO, L, D, out, s, scale, causal, st)
+           : dtype == DT_F16 ? dq_d<f16_t, DIRECT>(Q, K, V, dO, L, D, out, s, scale, causal, st)
+                             : dq_d<float, DIRECT>(Q, K, V, dO, L, D, out, s, scale, causal, st);
 }
 
 }  // namespace
@@ -280,9 +300,13 @@ hipError_t launch_bwd_dkdv_simt(int dtype, const void* Q, const void* K, const v
 hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st) {
-    return dtype == DT_BF16   ? dq_d<bf16_t>(Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
-           : dtype == DT_F16  ? dq_d<f16_t>(Q, K, V, dO, L, D, dq_accum, s, scale, causal, st)
-                              : dq_d<float>(Q, K, V, dO, L, D, dq_accum, s, scale, causal, st);
+    return dq_any<false>(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal, st);
+}
+
+hipError_t launch_bwd_dq_simt_direct(int dtype, const void* Q, const void* K, const void* V,
+                                     const void* dO, const float* L, const float* D, void* dQ,
+                                     Shape s, float scale, bool causal, hipStream_t st) {
+    return dq_any<true>(dtype, Q, K, V, dO, L, D, dQ, s, scale, causal, st);
 }
 
 }  // namespace fa

@@ -34,6 +34,10 @@ hipError_t launch_bwd_dkdv_simt(int dtype, const void* Q, const void* K, const v
 hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);
+// The same dQ pass writing dQ = scale * dq_accum in the element type directly.
+hipError_t launch_bwd_dq_simt_direct(int dtype, const void* Q, const void* K, const void* V,
+                                     const void* dO, const float* L, const float* D, void* dQ,
+                                     Shape s, float scale, bool causal, hipStream_t st);
 
 // Matrix-core backward, bf16 or fp16 (dtype), head dim 64 or 128: key-outer
 // dK/dV pass and query-outer dQ pass (dq_accum rows written once, unscaled).
@@ -43,5 +47,9 @@ hipError_t launch_bwd_dkdv_mfma(int dtype, const void* Q, const void* K, const v
 hipError_t launch_bwd_dq_mfma(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);
+// The same dQ pass writing dQ = scale * dq_accum in the element type directly.
+hipError_t launch_bwd_dq_mfma_direct(int dtype, const void* Q, const void* K, const void* V,
+                                     const void* dO, const float* L, const float* D, void* dQ,
+                                     Shape s, float scale, bool causal, hipStream_t st);
 
 }  // namespace fa

@@ -33,9 +33,11 @@
  *              caller, at least 16-byte aligned, each to a buffer holding at
  *              least the elements its layout implies for the call's B, H, N
  *              and d (the library cannot check this: a smaller buffer is read
- *              or written out of bounds).  Outputs must not alias inputs.  The library allocates nothing and keeps no mutable
- *              global state; calls on different streams may run concurrently
- *              as long as their buffers are disjoint.
+ *              or written out of bounds).  Outputs must not alias inputs.
+ *              The library allocates nothing; its only mutable global state
+ *              is fa_bwd_noalloc's static scratch array (see there).  Calls
+ *              on different streams may run concurrently as long as their
+ *              buffers are disjoint (fa_bwd_noalloc calls excepted).
  *   Stream     `stream` is a hipStream_t passed as void*; NULL is the null
  *              stream.  Every call only enqueues work and returns; the caller
  *              synchronises.
@@ -63,8 +65,13 @@ typedef enum {
     FA_OK = 0,
     FA_EINVAL = 1,
     FA_EUNSUPPORTED = 2,
-    FA_EHIP = 3
+    FA_EHIP = 3,
+    FA_ESCRATCH = 4  /* fa_bwd_noalloc only: B * H * N above FA_NOALLOC_MAX_ROWS */
 } fa_status_t;
+
+/* Rows (B * H * N) that fa_bwd_noalloc's static scratch array holds: 16 MiB of
+ * fp32 per GPU. */
+#define FA_NOALLOC_MAX_ROWS (1 << 22)
 
 /*
  * fa_fwd_lse -- attention forward producing O and the logsumexp L that the
@@ -163,6 +170,30 @@ int fa_bwd_dq(int dtype, const void* Q, const void* K, const void* V,
  */
 int fa_bwd_convert_dq(int dtype, const float* dq_accum, void* dQ,
                       int B, int H, int N, int d, float scale, void* stream);
+
+/*
+ * fa_bwd_noalloc -- the whole backward (fa_bwd_preprocess, fa_bwd and
+ * fa_bwd_convert_dq in one call) without any device allocation and without a
+ * caller workspace, for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   D lives in a static device array of the library (FA_NOALLOC_MAX_ROWS fp32,
+ *   one per GPU, kept until the process ends; its address is looked up on the
+ *   first call on each device); dq_accum is not needed: the dQ pass writes
+ *   dQ = scale * (sum_j dS_ij K_j) in the element type itself, the same values
+ *   fa_bwd_convert_dq makes of dq_accum.  Outputs equal those of the three
+ *   calls bit for bit.
+ *   Calls of one process that overlap on one GPU (concurrent streams or
+ *   threads) race on that GPU's scratch array: serialise them.  Sequential
+ *   calls on one stream are safe; every call rewrites the D rows it reads.
+ *   in : Q, K, V, O, dO [B,H,N,d] dtype; L [B,H,N] fp32
+ *   out: dQ, dK, dV [B,H,N,d] dtype
+ *   errors: as fa_bwd; FA_ESCRATCH when B * H * N > FA_NOALLOC_MAX_ROWS.
+ */
+int fa_bwd_noalloc(int dtype, const void* Q, const void* K, const void* V,
+                   const void* O, const void* dO, const float* L,
+                   void* dQ, void* dK, void* dV,
+                   int B, int H, int N, int d, float scale, int causal,
+                   void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -87,6 +87,25 @@ def test_unsupported_head_dim(d):
     assert lib.fa_bwd_convert_dq(1, p, p, 1, 1, 8, d, 0.1, None) == fa.FA_EUNSUPPORTED
 
 
+def test_noalloc_validates_arguments_and_size():
+    """fa_bwd_noalloc checks its arguments like fa_bwd and refuses problems
+    whose D does not fit its static scratch array (FA_ESCRATCH), before any
+    device work."""
+    lib = fa.load()
+    p = ALIGNED
+    call = lambda dtype=1, q=p, B=1, H=1, N=8, d=64, sc=0.125: lib.fa_bwd_noalloc(
+        dtype, q, p, p, p, p, p, p, p, p, B, H, N, d, sc, 0, None)
+    assert call(q=None) == fa.FA_EINVAL
+    assert call(q=p + 4) == fa.FA_EINVAL
+    assert call(dtype=9) == fa.FA_EINVAL
+    assert call(sc=0.0) == fa.FA_EINVAL
+    assert call(d=96) == fa.FA_EUNSUPPORTED
+    rows = fa.FA_NOALLOC_MAX_ROWS
+    assert call(B=1, H=4, N=rows // 4 + 1, d=16) == fa.FA_ESCRATCH
+    assert call(B=2, H=64, N=32768 + 1, d=128) == fa.FA_ESCRATCH
+    assert "FA_NOALLOC_MAX_ROWS" in fa.fa_strerror(fa.FA_ESCRATCH)
+
+
 def test_split_passes_validate_arguments():
     lib = fa.load()
     p = ALIGNED
@@ -123,6 +142,7 @@ calls = {
     "fa_bwd_dkdv": lambda d, t: lib.fa_bwd_dkdv(t, p, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 0, None),
     "fa_bwd_dq": lambda d, t: lib.fa_bwd_dq(t, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 1, None),
     "fa_bwd_convert_dq": lambda d, t: lib.fa_bwd_convert_dq(t, p, p, 1, 2, 40, d, f(0.125), None),
+    "fa_bwd_noalloc": lambda d, t: lib.fa_bwd_noalloc(t, p, p, p, p, p, p, p, p, p, 1, 2, 40, d, f(0.125), 1, None),
 }
 for nm, call in calls.items():
     for d in (16, 32, 64, 128):
@@ -145,7 +165,7 @@ def test_every_entry_point_reports_no_device():
     if out["device"]:
         pytest.skip("a device is present; the no-device path cannot be exercised here")
     results = {k: v for k, v in out.items() if "/" in k}
-    assert len(results) == 7 * 4 * 3
+    assert len(results) == 8 * 4 * 3
     for k, (rc, hip_err) in results.items():
         assert rc == fa.FA_EHIP, (k, rc)
         assert hip_err != 0, k
