@@ -44,6 +44,12 @@ hipError_t launch_bwd_dq_simt_direct(int dtype, const void* Q, const void* K, co
 hipError_t launch_bwd_dkdv_mfma(int dtype, const void* Q, const void* K, const void* V,
                                 const void* dO, const float* L, const float* D, void* dK,
                                 void* dV, Shape s, float scale, bool causal, hipStream_t st);
+// Both matrix-core passes in one launch (fa_bwd): dQ-pass work items first,
+// then dK/dV-pass work items, in one grid.
+hipError_t launch_bwd_fused_mfma(int dtype, const void* Q, const void* K, const void* V,
+                                 const void* dO, const float* L, const float* D, float* dq_accum,
+                                 void* dK, void* dV, Shape s, float scale, bool causal,
+                                 hipStream_t st);
 hipError_t launch_bwd_dq_mfma(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);

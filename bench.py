@@ -2,8 +2,9 @@
 """Benchmark of the FlashAttention-2 backward on one MI355X.
 
 A step is one pass of the whole backward hot path -- fa_bwd_preprocess (D),
-the two passes of fa_bwd (fa_bwd_dq, then fa_bwd_dkdv) and fa_bwd_convert_dq --
-over one batch of synthetic inputs already resident in HBM.  The forward that
+fa_bwd (the dQ and dK/dV passes; one launch on the matrix cores) and
+fa_bwd_convert_dq -- over one batch of synthetic inputs already resident in
+HBM.  The forward that
 produces O and L runs once before timing and is not timed.
 
 The line's value is the bench shape, B=1 H=32 N=8192 d=128 bf16 (non-causal
@@ -35,15 +36,16 @@ PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 
 PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector: 256 CU x 2.4 GHz x 256 FLOP/clk
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention backward TFLOP/s (10·B·H·N²·d, halved causal) and % bf16 MFMA peak"
-MAIN_KERNEL_SOURCES = ["attention_fa_bwd_amd/csrc/bwd_dkdv.hip", "attention_fa_bwd_amd/csrc/bwd_dq.hip",
-                       "attention_fa_bwd_amd/csrc/bwd_simt.hip", "attention_fa_bwd_amd/csrc/mfma_common.hpp"]
+MAIN_KERNEL_SOURCES = ["attention_fa_bwd_amd/csrc/bwd_dkdv.hpp", "attention_fa_bwd_amd/csrc/bwd_dq.hpp",
+                       "attention_fa_bwd_amd/csrc/bwd_fused.hip", "attention_fa_bwd_amd/csrc/bwd_simt.hip",
+                       "attention_fa_bwd_amd/csrc/mfma_common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_main_traffic.json")
 PRIMARY = "h32_n8192_d128_bf16"
 # (workload, causal) of every timed configuration, in the order they run
 CONFIGS = [("n48_d16_fp32", False), ("n48_d16_fp32", True), ("h8_n1024_d64_bf16", False),
            ("h32_n8192_d128_bf16", False), ("h32_n8192_d128_bf16", True),
            ("b4_h16_n4000_d128_bf16_q4", True), ("h8_n32768_d128_bf16", True)]
-PASSES = ("fa_bwd_preprocess", "fa_bwd_dq", "fa_bwd_dkdv", "fa_bwd_convert_dq")
+STEP_CALLS = ("fa_bwd_preprocess", "fa_bwd", "fa_bwd_convert_dq")
 
 
 def parse(argv=None):
@@ -122,11 +124,11 @@ def calibrate_copy():
                       "launches": 5}))
 
 
-# Algorithmic FLOPs of each backward pass per (b, h), as a multiple of N^2 d
-# before the causal halving: the dK/dV pass recomputes S and dP and forms dV
-# and dK (4 of the 5 products), the dQ pass recomputes S and dP and forms dQ
-# (3 products).
-KERNEL_FLOP_FACTOR = {"fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
+# Algorithmic FLOPs per (b, h), as a multiple of N^2 d before the causal
+# halving: the dK/dV pass recomputes S and dP and forms dV and dK (4 of the 5
+# products), the dQ pass recomputes S and dP and forms dQ (3 products);
+# fa_bwd runs both (one launch on the matrix cores).
+KERNEL_FLOP_FACTOR = {"fa_bwd": 14.0, "fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
 
 
 def elem_bytes(wl) -> int:
@@ -176,29 +178,25 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    # one step: preprocess, dQ pass, dK/dV pass, convert (fa_bwd runs the two
-    # passes back to back; calling them separately lets events split them)
+    # one step: preprocess, fa_bwd (both passes), convert
     def step(evs=None):
         if evs:
             evs[0].record(stream)
         fa.fa_bwd_preprocess(o, do, D, stream)
         if evs:
             evs[1].record(stream)
-        fa.fa_bwd_dq(q, k, v, do, L, D, dqa, scale, causal, stream)
+        fa.fa_bwd(q, k, v, do, L, D, dqa, dk, dv, scale, causal, stream)
         if evs:
             evs[2].record(stream)
-        fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, scale, causal, stream)
-        if evs:
-            evs[3].record(stream)
         fa.fa_bwd_convert_dq(dqa, dq, scale, stream)
         if evs:
-            evs[4].record(stream)
+            evs[3].record(stream)
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # timed region: K whole steps; HIP events on the launch stream split it per kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -210,8 +208,8 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    split = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(PASSES)}
-    per_step = [e[0].elapsed_time(e[4]) for e in evs]
+    split = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(STEP_CALLS)}
+    per_step = [e[0].elapsed_time(e[3]) for e in evs]
     return {
         "ms_per_step": total_ms / steps,
         "step_ms": {"median": round(statistics.median(per_step), 4),
@@ -220,6 +218,32 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
         "kernel_ms": {k: statistics.fmean(v) for k, v in split.items()},
         "kernel_ms_min": {k: min(v) for k, v in split.items()},
     }
+
+
+def passes_alone(wl, causal: bool, inputs, reps: int = 5) -> dict:
+    """Each pass launched on its own (fa_bwd_dq, fa_bwd_dkdv), outside the
+    step: how fa_bwd's time splits between them."""
+    import torch
+
+    import attention_fa_bwd_amd as fa
+    q, k, v, do, o, L = inputs
+    B, H, N, d = q.shape
+    D = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dqa = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    dk, dv = torch.empty_like(q), torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    fa.fa_bwd_preprocess(o, do, D, stream)
+    bound, peak = compute_peak(wl)
+    out = {}
+    for name, fn in (("fa_bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, L, D, dqa, wl.scale, causal, stream)),
+                     ("fa_bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, wl.scale,
+                                                            causal, stream))):
+        ms = timed_reps(fn, reps)
+        kf = pass_flops(wl, causal, name)
+        out[name] = {"avg_launch_ms": round(ms, 5), "flop_per_launch": kf,
+                     "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
+                     "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4)}
+    return out
 
 
 def timed_reps(fn, reps: int = 5) -> float:
@@ -345,18 +369,18 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
     tflops = flops / (r["ms_per_step"] * 1e-3) / 1e12
     bound, peak = compute_peak(wl)
     kernels = {}
-    for kname in KERNEL_FLOP_FACTOR:
-        kf, ms = pass_flops(wl, causal, kname), r["kernel_ms"][kname]
-        kernels[kname] = {"avg_launch_ms": round(ms, 4), "flop_per_launch": kf,
-                          "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
-                          "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4)}
+    kf, ms = pass_flops(wl, causal, "fa_bwd"), r["kernel_ms"]["fa_bwd"]
+    kernels["fa_bwd"] = {"avg_launch_ms": round(ms, 5), "flop_per_launch": kf,
+                         "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
+                         "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4)}
     for kname, nbytes in hbm_kernel_bytes(wl).items():
         ms = r["kernel_ms"][kname]
         gbs = nbytes / (ms * 1e-3) / 1e9
-        kernels[kname] = {"avg_launch_ms": round(ms, 4), "bytes_per_launch": nbytes,
+        kernels[kname] = {"avg_launch_ms": round(ms, 5), "bytes_per_launch": nbytes,
                           "achieved_gbs": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
-    dom = max(KERNEL_FLOP_FACTOR, key=lambda n: r["kernel_ms"][n])
+    dom = "fa_bwd"   # the main step: far longer than preprocess and convert
     kd = kernels[dom]
+    alone = passes_alone(wl, causal, (q, k, v, do, o, L))
     out = {
         "workload": f"B={wl.B} H={wl.H} N={wl.N} d={wl.d} {wl.dtype}"
                     f"{' Q x %g' % wl.q_mult if wl.q_mult != 1.0 else ''} "
@@ -374,6 +398,7 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
                      "flop_per_launch": kd["flop_per_launch"],
                      "avg_launch_ms": kd["avg_launch_ms"]},
         "kernels": kernels,
+        "passes_alone": alone,
     }
     if with_extras:
         out.update(extras(wl, causal, (q, k, v, do), r["ms_per_step"], flops))

@@ -56,6 +56,7 @@ def test_flop_and_byte_models():
     f = wl.flops(False)
     assert f == 10 * 32 * 8192 ** 2 * 128 and wl.flops(True) == f / 2
     assert bench.pass_flops(wl, False, "fa_bwd_dkdv") == 0.8 * f
+    assert bench.pass_flops(wl, True, "fa_bwd") == 0.7 * f
     assert bench.pass_flops(wl, True, "fa_bwd_dq") == 0.3 * f
     rows = 32 * 8192
     b = bench.hbm_kernel_bytes(wl)
@@ -71,9 +72,9 @@ def test_traffic_record_matches_current_kernels():
     """The committed HBM-traffic record carries the hash of the kernel
     sources it was measured on; bench.py reports it only while they match."""
     rec = json.load(open(bench.TRAFFIC_FILE))
-    for key in ("fa_bwd_dkdv/h32_n8192_d128_bf16_full", "fa_bwd_dq/h32_n8192_d128_bf16_full"):
+    for key in ("fa_bwd/h32_n8192_d128_bf16_full", "fa_bwd/h32_n8192_d128_bf16_causal"):
         assert key in rec["entries"]
     if rec["kernel_source_hash"] == bench.kernel_source_hash():
-        assert bench.load_traffic("h32_n8192_d128_bf16", False, "fa_bwd_dkdv") > 0
+        assert bench.load_traffic("h32_n8192_d128_bf16", False, "fa_bwd") > 0
     else:
-        assert bench.load_traffic("h32_n8192_d128_bf16", False, "fa_bwd_dkdv") is None
+        assert bench.load_traffic("h32_n8192_d128_bf16", False, "fa_bwd") is None
