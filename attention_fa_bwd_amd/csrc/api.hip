@@ -1,7 +1,9 @@
 // api.hip -- the extern "C" entry points declared in include/fa_bwd.h:
 // argument validation, then one launcher per call.  No allocation; the only
-// global mutable state is the calling thread's last HIP error code and, for
-// fa_bwd_noalloc, the per-device address of its static scratch array.
+// global mutable state is the calling thread's last HIP error code, the CU
+// count of each device (queried once) and, for fa_bwd_noalloc, the per-device
+// address of its static scratch array.
+#include <atomic>
 #include <mutex>
 
 #include "../../include/fa_bwd.h"
@@ -12,6 +14,33 @@
 // name stands for the host-side shadow of the array, not a device address:
 // kernels get the address hipGetSymbolAddress returns for the current device.
 static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
+namespace fa {
+
+int resident_per_cu(const void* k, int threads) {
+    int per = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, k, threads, 0) != hipSuccess || per < 1)
+        return 1;
+    return per;
+}
+
+int persistent_grid(long long items, int per_cu) {
+    constexpr int kDevices = 64;
+    static std::atomic<int> cus[kDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    int c = dev < kDevices ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (c <= 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            return 0;
+        if (dev < kDevices) cus[dev].store(c, std::memory_order_relaxed);
+    }
+    const long long g = (long long)c * (per_cu < 1 ? 1 : per_cu);
+    return (int)(items < g ? items : g);
+}
+
+}  // namespace fa
 
 namespace {
 

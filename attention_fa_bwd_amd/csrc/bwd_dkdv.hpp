@@ -1,7 +1,7 @@
 // bwd_dkdv.hpp -- key-outer pass of the FA2 backward on gfx950 matrix cores:
 // dK and dV for bf16 and fp16, head dims 64 and 128.
 //
-// Method (FA2 chapter 16): one workgroup per (key block of 128 keys, head,
+// Method (FA2 chapter 16): one work item per (key block of 128 keys, head,
 // batch), key blocks outer and query tiles inner (sec 16.2); per query tile
 // S = scale Q K^T and P = exp(S - L) are recomputed (sec 16.4), dP = dO V^T,
 // dS = P (dP - D) with D from the preprocess (sec 16.1, sec 16.8 item 1), and
@@ -11,7 +11,9 @@
 // above the diagonal are never visited (sec 16.8 item 2).  dQ is produced by
 // the query-outer pass in bwd_dq.hip.
 //
-// gfx950 mapping: 8 waves, two per SIMD, in two roles that overlap on each
+// gfx950 mapping: a persistent grid (one workgroup per CU, each running a
+// fixed list of work items with their query tiles back to back, see
+// dkdv_run); 8 waves, two per SIMD, in two roles that overlap on each
 // SIMD (one wave's matrix-core work runs while the other computes or waits on
 // LDS):
 //   * score wave s owns key groups 2 (s % 2) and 2 (s % 2) + 1 (64 keys; K^T
@@ -229,7 +231,8 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
 // slabs (one per key group, each feeding two), read two steps ahead.
 // ob0 / ob1: the lane's transposing-read offsets of rows 4 h + (l % 16) / 4
 // and that + 8 in each d block (rows 16 t + ... share their swizzle).
-template <typename E, int DH>
+// FIRST: the tile is its work item's first; the accumulators start from zero.
+template <typename E, int DH, bool FIRST>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf, bool dk,
                                           f32x16_t (&acc)[2][DH / 32], const int (&ob0)[2],
                                           const int (&ob1)[2], int kg0, int l) {
@@ -259,100 +262,151 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
         for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
             for (int db = 0; db < 2; ++db)
-                acc[db][kg] = E::mma(a[t % 3][db], b[t % 3][kg], acc[db][kg]);
+                acc[db][kg] = E::mma(a[t % 3][db], b[t % 3][kg],
+                                     FIRST && t == 0 ? f32x16_t{} : acc[db][kg]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
+
+// Work item of the pass: key block k0 of head `head` (batch and head folded),
+// its first query tile and its number of query tiles.
+template <int DH, bool CAUSAL>
+struct KeyItem {
+    int head, k0, q_begin, ntiles;
+    __device__ __forceinline__ KeyItem(int work, int nwork, int nkb, int N) {
+        int kblk = work % nkb;
+        head = work / nkb;
+        if (CAUSAL) heavy_first_work(work, nwork, nkb, head, kblk);  // heaviest (first) key blocks first
+        k0 = kblk * BC;
+        q_begin = CAUSAL ? k0 : 0;  // causal: tiles wholly above the diagonal are skipped
+        ntiles = (N - q_begin + BR - 1) / BR;
+    }
+    __device__ __forceinline__ long long hoff(int N) const { return (long long)head * N * DH; }
+};
+
+// A position in a workgroup's run of tiles: tile p of the item of round m.
+template <int DH, bool CAUSAL>
+struct KeyCursor {
+    int m, p;
+    KeyItem<DH, CAUSAL> it;
+    __device__ __forceinline__ bool valid(const Run& r) const { return m < r.m1; }
+    __device__ __forceinline__ void advance(const Schedule& s, const Run& r, int nwork, int nkb,
+                                            int N) {
+        if (++p == it.ntiles) {
+            p = 0;
+            if (++m < r.m1) it = KeyItem<DH, CAUSAL>(r.item(s, m), nwork, nkb, N);
+        }
+    }
+};
+
+// The workgroup's run of work items (rounds [run.m0, run.m1) of the
+// schedule), their query tiles back to back: tile g of the run is scored in
+// phase g, staged in phase g - 1 and reduced into dK / dV in phase g + 1,
+// whether or not it starts a new item, so that an item's first tiles overlap
+// the previous item's last ones.  At an item boundary the score waves load the
+// next item's K^T and V^T fragments right after their last product with the
+// old ones, and the gradient waves store the finished dK / dV rows just
+// before the first products of the next item.
 template <typename E, int DH, bool CAUSAL>
-__device__ __forceinline__ void dkdv_work(
+__device__ __forceinline__ void dkdv_run(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
     const e16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
-    e16_t* __restrict__ dK, e16_t* __restrict__ dV, int N, int nkb, float scale, int bid, int nwork,
-    unsigned char* smem) {
+    e16_t* __restrict__ dK, e16_t* __restrict__ dV, int N, int nkb, float scale,
+    const Schedule& sch, const Run& run, int nwork, unsigned char* smem) {
     using PL = Plan<DH>;
+    using Item = KeyItem<DH, CAUSAL>;
     constexpr int NI = PL::NI;
     constexpr int KG = DH / 32;  // key groups per gradient wave
-
-    const int work = xcd_work_item(bid, nwork);
-    int head = work / nkb, kblk = work % nkb;
-    if (CAUSAL) heavy_first_work(work, nwork, nkb, head, kblk);  // heaviest (first) key blocks first
-    const int k0 = kblk * BC;
-    const long long hoff = (long long)head * N * DH;
-    const e16_t* Qh = Q + hoff;
-    const e16_t* dOh = dO + hoff;
-    const float* Lh = Lg + (long long)head * N;
-    const float* Dh = Dg + (long long)head * N;
+    if (run.m0 >= run.m1) return;
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
     const bool score = wave < 4;
     const int r4 = wave & 3;  // key group (score) or d block (gradient)
-
-    const int q_begin = CAUSAL ? k0 : 0;
-    const int ntiles = (N - q_begin + BR - 1) / BR;
-    const int nmask = CAUSAL ? BC / BR : 0;  // tiles that cross the diagonal
     const float sc = scale * kLog2e;
+    const Item first(run.item(sch, run.m0), nwork, nkb, N);
 
-    stage_rows<BR, NWAVE, DH>(smem + PL::OFF_Q, Qh, q_begin, N, wave, l);
-    stage_rows<BR, NWAVE, DH>(smem + PL::OFF_DO, dOh, q_begin, N, wave, l);
+    // tile 0 of the run, by all waves
+    stage_rows<BR, NWAVE, DH>(smem + PL::OFF_Q, Q + first.hoff(N), first.q_begin, N, wave, l);
+    stage_rows<BR, NWAVE, DH>(smem + PL::OFF_DO, dO + first.hoff(N), first.q_begin, N, wave, l);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // Phase p (one barrier each, ntiles + 1 phases): score waves work on tile p;
-    // gradient waves stage tile p + 1 (the score waves' only memory traffic is
-    // L and D, so their waits never cover the staging copies) and work on
-    // tile p - 1.  Each role has its own loop so that its registers never
-    // coexist with the other role's.
+    // Phase g (one barrier each, one more than the run has tiles): score
+    // waves work on tile g; gradient waves stage tile g + 1 (the score waves'
+    // only memory traffic is L, D and, at item boundaries, K and V, so their
+    // waits never cover the staging copies) and work on tile g - 1.  Each role
+    // has its own loop so that its registers never coexist with the other
+    // role's.  Tile g uses Q / dO buffer g % 3 and P / dS buffer g % 2.
     if (score) {
         const int kp = r4 & 1, qh = r4 >> 1;  // key pair, query half of each tile
-        v16x8_t kt[2][NI], vt[2][NI];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int kk = k0 + 64 * kp + 32 * c + n;
-            const int keyc = kk < N ? kk : N - 1;  // clamped: finite data, outputs not stored
-#pragma unroll
-            for (int dk = 0; dk < NI; ++dk) {
-                kt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * DH + 16 * dk + 8 * h));
-                vt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * DH + 16 * dk + 8 * h));
-            }
-        }
-        // row statistic of this wave's rows in tile p in st (L on lane half
-        // 0, D on half 1), that of tile p + 1 fetched during step p
-        const float* stat = (h ? Dh : Lh) + 32 * qh;
         const float fac = h ? -1.f : -1.f / scale;
-        auto fetch1 = [&](int qn) { return fetch_stat(stat, qn + n, N - 32 * qh); };
         int so[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) so[i] = tile_off<PL::ROWB>(n, 32 * i + 16 * h);
-        float st = fetch1(q_begin);
-        // diagonal tiles (causal only) first, then the rest; the waits before
-        // each barrier cover only LDS traffic, so the next tile's statistic
-        // stays in flight across it
-        int p = 0;
-        for (; p < min(nmask, ntiles); ++p) {
-            const int q0 = q_begin + p * BR;
-            const float nx = fetch1(q0 + BR);
-            if (q0 + BR > N)
-                score_step<E, DH, true, true>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
-            else
-                score_step<E, DH, false, true>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
-            st = nx;
-            __builtin_amdgcn_s_waitcnt(kLgkmOnly);
-            __syncthreads();
-        }
-        for (; p <= ntiles; ++p) {
-            if (p < ntiles) {
-                const int q0 = q_begin + p * BR;
-                const float nx = fetch1(q0 + BR);
-                if (q0 + BR > N)
-                    score_step<E, DH, true, false>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
-                else
-                    score_step<E, DH, false, false>(smem, p % 3, p & 1, q0, N, k0, sc, fac, st, kt, vt, so, kp, qh, l);
-                st = nx;
+        v16x8_t kt[2][NI], vt[2][NI];
+        auto load_kv = [&](const Item& it) {
+            const long long hoff = it.hoff(N);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const int kk = it.k0 + 64 * kp + 32 * c + n;
+                const int keyc = kk < N ? kk : N - 1;  // clamped: finite data, outputs not stored
+#pragma unroll
+                for (int dk = 0; dk < NI; ++dk) {
+                    kt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(K + hoff + (long long)keyc * DH + 16 * dk + 8 * h));
+                    vt[c][dk] = as_v16x8(*reinterpret_cast<const uint4*>(V + hoff + (long long)keyc * DH + 16 * dk + 8 * h));
+                }
             }
-            __builtin_amdgcn_s_waitcnt(kLgkmOnly);
-            __syncthreads();
+        };
+        // row statistic of this wave's rows (L on lane half 0, D on half 1),
+        // that of the next tile (possibly the next item's first) fetched
+        // during each step
+        auto stat_of = [&](const Item& it) {
+            return (h ? Dg : Lg) + (long long)it.head * N + 32 * qh;
+        };
+        Item it = first;
+        load_kv(it);
+        const float* stat = stat_of(it);
+        float st = fetch_stat(stat, it.q_begin + n, N - 32 * qh);
+        int qb = 0, pb = 0;
+        for (int m = run.m0; m < run.m1; ++m) {
+            const bool more = m + 1 < run.m1;
+            const Item nxt = more ? Item(run.item(sch, m + 1), nwork, nkb, N) : it;
+            const float* nstat = stat_of(nxt);
+            // tiles crossing the diagonal (causal only) first, then the rest;
+            // the waits before each barrier cover only LDS traffic, so the
+            // next statistic (and the next item's K and V) stay in flight
+            // across it
+            const int nmask = CAUSAL ? BC / BR : 0;
+            for (int p = 0; p < it.ntiles; ++p) {
+                const int q0 = it.q_begin + p * BR;
+                const bool last = p + 1 == it.ntiles;
+                const float nx = fetch_stat(last ? nstat : stat, (last ? nxt.q_begin : q0 + BR) + n,
+                                            N - 32 * qh);
+                const bool ragged = q0 + BR > N;
+                if (CAUSAL && p < nmask) {
+                    if (ragged)
+                        score_step<E, DH, true, true>(smem, qb, pb, q0, N, it.k0, sc, fac, st, kt, vt, so, kp, qh, l);
+                    else
+                        score_step<E, DH, false, true>(smem, qb, pb, q0, N, it.k0, sc, fac, st, kt, vt, so, kp, qh, l);
+                } else {
+                    if (ragged)
+                        score_step<E, DH, true, false>(smem, qb, pb, q0, N, it.k0, sc, fac, st, kt, vt, so, kp, qh, l);
+                    else
+                        score_step<E, DH, false, false>(smem, qb, pb, q0, N, it.k0, sc, fac, st, kt, vt, so, kp, qh, l);
+                }
+                st = nx;
+                if (last && more) load_kv(nxt);
+                qb = qb == 2 ? 0 : qb + 1;
+                pb ^= 1;
+                __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+                __syncthreads();
+            }
+            it = nxt;
+            stat = nstat;
         }
+        __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+        __syncthreads();  // the gradient waves' last tile
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
@@ -364,10 +418,13 @@ __device__ __forceinline__ void dkdv_work(
     const int db0 = DH == 128 ? 2 * (r4 & 1) : 0;  // first 32-row block of d
     const int kg0 = DH == 128 ? 0 : 2 * (r4 & 1);  // first key group
     f32x16_t acc[2][KG];
+    auto zero = [](f32x16_t(&a)[2][KG]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < KG; ++j) acc[i][j] = f32x16_t{};
+            for (int j = 0; j < KG; ++j) a[i][j] = f32x16_t{};
+    };
+    zero(acc);
     const TileCopier<BR, NWAVE / 2, DH> cp(r4, l);
     const uint32_t lds0 = lds_addr(smem);
     int ob0[2], ob1[2];
@@ -380,44 +437,67 @@ __device__ __forceinline__ void dkdv_work(
             ob1[db] = tile_off<PL::ROWB>(x + 8, colb);
         }
     }
-    for (int p = 0; p <= ntiles; ++p) {
-        // copies of tile p + 1 first: they need the whole phase to land.  In
-        // the last two phases the buffer they fill is read by no one; they
-        // are issued all the same (rows clamped into range) rather than
-        // behind a branch.
-        const int qn = q_begin + (p + 1) * BR;
-        const uint32_t lq = lds0 + PL::OFF_Q + ((p + 1) % 3) * PL::TILE;
+    // acc[db][kg] holds dV^T or dK^T for keys k0 + 32 (kg0 + kg) + n, rows of
+    // d 32 (db0 + db) + 8 (r / 4) + 4 h + r % 4
+    e16_t* const out = is_dk ? dK : dV;
+    const float osc = is_dk ? scale : 1.f;
+    auto epilogue = [&](const Item& it) {
+        const long long hoff = it.hoff(N);
 #pragma unroll
-        for (int j = 0; j < cp.SLICES; ++j) {
-            cp.copy(j, Qh, qn, N, lq);
-            cp.copy(j, dOh, qn, N, lq + (PL::OFF_DO - PL::OFF_Q));
+        for (int kg = 0; kg < KG; ++kg) {
+            const int kk = it.k0 + 32 * (kg0 + kg) + n;
+            if (kk >= N) continue;
+            e16_t* row = out + hoff + (long long)kk * DH;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int d0 = 32 * (db0 + db) + 8 * a4 + 4 * h;
+                    const int r = 4 * a4;
+                    uint2 v;
+                    v.x = E::pack2(acc[db][kg][r] * osc, acc[db][kg][r + 1] * osc);
+                    v.y = E::pack2(acc[db][kg][r + 2] * osc, acc[db][kg][r + 3] * osc);
+                    *reinterpret_cast<uint2*>(row + d0) = v;
+                }
         }
-        if (p >= 1) grad_step<E, DH>(smem, (p - 1) % 3, (p - 1) & 1, is_dk, acc, ob0, ob1, kg0, l);
+    };
+    KeyCursor<DH, CAUSAL> stg{run.m0, 0, first};  // the tile staged last
+    KeyCursor<DH, CAUSAL> grd{run.m0, 0, first};  // the next tile to reduce
+    Item acc_it = first;                          // the item the accumulators belong to
+    int qb = 0, pb = 0;                           // buffers of tile g
+    for (int g = 0;; ++g) {
+        // copies of tile g + 1 first: they need the whole phase to land
+        stg.advance(sch, run, nwork, nkb, N);
+        const int qbn = qb == 2 ? 0 : qb + 1;
+        if (stg.valid(run)) {
+            const long long hoff = stg.it.hoff(N);
+            const int qn = stg.it.q_begin + stg.p * BR;
+            const uint32_t lq = lds0 + PL::OFF_Q + qbn * PL::TILE;
+#pragma unroll
+            for (int j = 0; j < cp.SLICES; ++j) {
+                cp.copy(j, Q + hoff, qn, N, lq);
+                cp.copy(j, dO + hoff, qn, N, lq + (PL::OFF_DO - PL::OFF_Q));
+            }
+        }
+        if (g >= 1) {
+            const int qbp = qb == 0 ? 2 : qb - 1;
+            if (grd.p == 0 && grd.m > run.m0) {
+                // the tile starts a new item: the previous item's sums are
+                // complete; store them, then start from zero
+                epilogue(acc_it);
+                zero(acc);
+            }
+            if (grd.p == 0) acc_it = grd.it;
+            grad_step<E, DH, false>(smem, qbp, pb ^ 1, is_dk, acc, ob0, ob1, kg0, l);
+            grd.advance(sch, run, nwork, nkb, N);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (!grd.valid(run)) break;
+        qb = qbn;
+        pb ^= 1;
     }
-
-    // epilogue: acc[db][kg] holds dV^T or dK^T for keys k0 + 32 (kg0 + kg) + n,
-    // rows of d 32 (db0 + db) + 8 (r / 4) + 4 h + r % 4
-    e16_t* out = is_dk ? dK : dV;
-    const float osc = is_dk ? scale : 1.f;
-#pragma unroll
-    for (int kg = 0; kg < KG; ++kg) {
-        const int kk = k0 + 32 * (kg0 + kg) + n;
-        if (kk >= N) continue;
-        e16_t* row = out + hoff + (long long)kk * DH;
-#pragma unroll
-        for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int d0 = 32 * (db0 + db) + 8 * a4 + 4 * h;
-                const int r = 4 * a4;
-                uint2 v;
-                v.x = E::pack2(acc[db][kg][r] * osc, acc[db][kg][r + 1] * osc);
-                v.y = E::pack2(acc[db][kg][r + 2] * osc, acc[db][kg][r + 3] * osc);
-                *reinterpret_cast<uint2*>(row + d0) = v;
-            }
-    }
+    epilogue(acc_it);
 }
 
 }  // namespace dkvp

@@ -5,14 +5,15 @@
 // against a second pass.  On MI355X the fp32 atomics run at about 340 G/s
 // (all of them execute beyond the L2), so one partial per (key block, query
 // tile) caps the whole backward far below the matrix-core rate.  This pass
-// instead gives each workgroup 256 query rows and loops over all key blocks,
+// instead gives each work item 256 query rows and loops over all key blocks,
 // recomputing S = scale Q K^T, P = exp(S - L) (sec 16.4), dP = dO V^T and
 // dS = P (dP - D) (sec 16.1), and accumulating dQ = dS K in registers; each
 // dq_accum row is written once, with plain stores.  Under the causal mask the
 // key loop stops at the diagonal (sec 16.8 item 2).
 //
-// gfx950 mapping: 8 waves, two per SIMD, in two roles that overlap on each
-// SIMD:
+// gfx950 mapping: a persistent grid (one workgroup per CU, each running a
+// fixed list of work items with their key blocks back to back, see dq_run);
+// 8 waves, two per SIMD, in two roles that overlap on each SIMD:
 //   * score waves 0..3 own queries [64 s, 64 s + 64) of the block as two
 //     groups of 32; their Q^T and dO^T B-operand fragments (d / 16 of each
 //     per group), L and D stay in registers.  Per key block of 32 they form S^T = K Q^T and
@@ -258,72 +259,93 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int kbuf, i
     }
 }
 
+// Work item of the pass: query block q0 of head `head` (batch and head
+// folded) and its number of key blocks.
+template <int DH, bool CAUSAL>
+struct QueryItem {
+    int head, q0, nblk;
+    __device__ __forceinline__ QueryItem(int work, int nwork, int nqb, int N) {
+        int qblk = work % nqb;
+        head = work / nqb;
+        if (CAUSAL) {  // heaviest (last) query blocks first
+            heavy_first_work(work, nwork, nqb, head, qblk);
+            qblk = nqb - 1 - qblk;
+        }
+        q0 = qblk * BQ;
+        const int kend = CAUSAL ? min(N, q0 + BQ) : N;  // causal: the loop stops at the diagonal
+        nblk = (kend + BK - 1) / BK;
+    }
+    __device__ __forceinline__ long long hoff(int N) const { return (long long)head * N * DH; }
+};
+
+// A position in a workgroup's run of key blocks: block p of the item of round m.
+template <int DH, bool CAUSAL>
+struct QueryCursor {
+    int m, p;
+    QueryItem<DH, CAUSAL> it;
+    __device__ __forceinline__ bool valid(const Run& r) const { return m < r.m1; }
+    __device__ __forceinline__ void advance(const Schedule& s, const Run& r, int nwork, int nqb,
+                                            int N) {
+        if (++p == it.nblk) {
+            p = 0;
+            if (++m < r.m1) it = QueryItem<DH, CAUSAL>(r.item(s, m), nwork, nqb, N);
+        }
+    }
+};
+
+// The workgroup's run of work items (rounds [run.m0, run.m1) of the
+// schedule), their key blocks back to back: block g of the run is staged
+// during phase g - 2, scored in phase g and reduced into dQ in phase g + 1,
+// whether or not it starts a new item, so that an item's first blocks overlap
+// the previous item's last ones.  At an item boundary the score waves load the
+// next item's Q^T and dO^T fragments, L and D right after their last product
+// with the old ones, and the gradient waves store the finished dQ rows just
+// before the first products of the next item.
 // DIRECT: instead of the unscaled fp32 dq_accum, write dQ = scale * acc in the
 // element type (round to nearest even), exactly what the convert step makes of
 // dq_accum; out is then the dQ tensor.
 template <typename E, int DH, bool CAUSAL, bool DIRECT>
-__device__ __forceinline__ void dq_work(
+__device__ __forceinline__ void dq_run(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
     const e16_t* __restrict__ dO, const float* __restrict__ Lg, const float* __restrict__ Dg,
-    void* __restrict__ dq_out, int N, int nqb, float scale, int bid, int nwork,
-    unsigned char* smem) {
+    void* __restrict__ dq_out, int N, int nqb, float scale, const Schedule& sch, const Run& run,
+    int nwork, unsigned char* smem) {
     using PL = Plan<DH>;
+    using Item = QueryItem<DH, CAUSAL>;
+    using Cursor = QueryCursor<DH, CAUSAL>;
     constexpr int NI = PL::NI;
     constexpr int QGW = DH / 32;  // query groups per gradient wave
-
-    const int work = xcd_work_item(bid, nwork);
-    int head = work / nqb, qblk = work % nqb;
-    if (CAUSAL) {  // heaviest (last) query blocks first
-        heavy_first_work(work, nwork, nqb, head, qblk);
-        qblk = nqb - 1 - qblk;
-    }
-    const int q0 = qblk * BQ;
-    const long long hoff = (long long)head * N * DH;
-    const e16_t* Kh = K + hoff;
-    const e16_t* Vh = V + hoff;
+    if (run.m0 >= run.m1) return;
 
     const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, h = l >> 5, n = l & 31;
     const bool score = wave < 4;
-    const int r4 = wave & 3;             // query pair of groups (score) or d block (gradient)
-
-    const int kend = CAUSAL ? min(N, q0 + BQ) : N;
-    const int nblk = (kend + BK - 1) / BK;
+    const int r4 = wave & 3;  // query pair of groups (score) or d block (gradient)
     const float sc = scale * kLog2e;
+    const Item first(run.item(sch, run.m0), nwork, nqb, N);
 
-    // blocks 0 and 1 up front; block p + 2 is copied during phase p
-    // (one 1 KiB slice per wave: all eight waves at d = 128, four at d = 64)
+    // blocks 0 and 1 of the run up front (one 1 KiB slice per wave: all eight
+    // waves at d = 128, four at d = 64); block g + 2 is copied during phase g
+    Cursor stg{run.m0, 0, first};  // the block staged last
     constexpr int SW = PL::TILE / 1024 < NWAVE ? PL::TILE / 1024 : NWAVE;
     if (SW == NWAVE || wave < SW) {
-        stage_rows<BK, SW, DH>(smem + PL::OFF_K, Kh, 0, N, wave, l);
-        stage_rows<BK, SW, DH>(smem + PL::OFF_V, Vh, 0, N, wave, l);
-        if (nblk > 1) {
-            stage_rows<BK, SW, DH>(smem + PL::OFF_K + PL::TILE, Kh, BK, N, wave, l);
-            stage_rows<BK, SW, DH>(smem + PL::OFF_V + PL::TILE, Vh, BK, N, wave, l);
-        }
+        stage_rows<BK, SW, DH>(smem + PL::OFF_K, K + first.hoff(N), 0, N, wave, l);
+        stage_rows<BK, SW, DH>(smem + PL::OFF_V, V + first.hoff(N), 0, N, wave, l);
+    }
+    stg.advance(sch, run, nwork, nqb, N);
+    if (stg.valid(run) && (SW == NWAVE || wave < SW)) {
+        const long long hoff = stg.it.hoff(N);
+        stage_rows<BK, SW, DH>(smem + PL::OFF_K + PL::TILE, K + hoff, stg.p * BK, N, wave, l);
+        stage_rows<BK, SW, DH>(smem + PL::OFF_V + PL::TILE, V + hoff, stg.p * BK, N, wave, l);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    // Phase p (one barrier each, nblk + 1 phases): score waves work on block p;
-    // gradient waves copy block p + 2 and work on block p - 1 (the score
-    // waves' MFMA work is twice theirs).  Each role has its own loop so their
-    // registers never coexist.
+    // Phase g (one barrier each, one more than the run has blocks): score
+    // waves work on block g; gradient waves copy block g + 2 and work on
+    // block g - 1 (the score waves' MFMA work is twice theirs).  Each role has
+    // its own loop so their registers never coexist.  Block g uses K buffer
+    // g % NKB, V buffer g % NVB and dS buffer g % 2.
     if (score) {
-        const int qw = q0 + 64 * r4;     // this wave's first query
-        const int qa = qw + n;           // this lane's query in group 0 (group 1: + 32)
-        v16x8_t qt[2][NI], gt[2][NI];
-        float Lq[2], Dq[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int qc = qa + 32 * g < N ? qa + 32 * g : N - 1;  // clamped: finite, not stored
-#pragma unroll
-            for (int dk = 0; dk < NI; ++dk) {
-                qt[g][dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * DH + 16 * dk + 8 * h));
-                gt[g][dk] = as_v16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * DH + 16 * dk + 8 * h));
-            }
-            Lq[g] = Lg[(long long)head * N + qc] * kLog2e;
-            Dq[g] = Dg[(long long)head * N + qc];
-        }
         int so[NI];
 #pragma unroll
         for (int i = 0; i < NI; ++i) so[i] = tile_off<PL::ROWB>(n, 32 * i + 16 * h);
@@ -332,33 +354,67 @@ __device__ __forceinline__ void dq_work(
         // lane's query split into three bf16 terms on those k-slots (about
         // 2^-26 relative), so the product broadcasts -D down the key rows.
         const v16x8_t ones = as_v16x8(h ? make_uint4(0, 0, 0, 0) : make_uint4(0x3F803F80u, 0x00003F80u, 0, 0));
-        v16x8_t bD[2];
+        v16x8_t qt[2][NI], gt[2][NI];
+        float Lraw[2], Draw[2];
+        // the item's fragments, L and D (used only from its first block on,
+        // so that the loads overlap the previous item's last block)
+        auto load_q = [&](const Item& it) {
+            const long long hoff = it.hoff(N);
+            const int qa = it.q0 + 64 * r4 + n;
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const float u = -Dq[g];
-            const float hi = (float)(__bf16)u;
-            const float r1 = u - hi;
-            const float mid = (float)(__bf16)r1;
-            bD[g] = as_v16x8(h ? make_uint4(0, 0, 0, 0)
-                               : make_uint4(pack_bf16x2(hi, mid), pack_bf16x2(r1 - mid, 0.f), 0, 0));
-        }
-        // blocks needing no mask for any of this wave's queries
-        const int full = CAUSAL ? min(qw / BK, N / BK) : N / BK;
-        for (int p = 0; p <= nblk; ++p) {
-            if (p < nblk) {
+            for (int g = 0; g < 2; ++g) {
+                const int qc = qa + 32 * g < N ? qa + 32 * g : N - 1;  // clamped: finite, not stored
+#pragma unroll
+                for (int dk = 0; dk < NI; ++dk) {
+                    qt[g][dk] = as_v16x8(*reinterpret_cast<const uint4*>(Q + hoff + (long long)qc * DH + 16 * dk + 8 * h));
+                    gt[g][dk] = as_v16x8(*reinterpret_cast<const uint4*>(dO + hoff + (long long)qc * DH + 16 * dk + 8 * h));
+                }
+                Lraw[g] = Lg[(long long)it.head * N + qc];
+                Draw[g] = Dg[(long long)it.head * N + qc];
+            }
+        };
+        Item it = first;
+        load_q(it);
+        int gb = 0;  // the run's block index g
+        for (int m = run.m0; m < run.m1; ++m) {
+            const bool more = m + 1 < run.m1;
+            const int qw = it.q0 + 64 * r4;  // this wave's first query
+            const int qa = qw + n;           // this lane's query in group 0 (group 1: + 32)
+            float Lq[2], Dq[2];
+            v16x8_t bD[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                Lq[g] = Lraw[g] * kLog2e;
+                Dq[g] = Draw[g];
+                const float u = -Dq[g];
+                const float hi = (float)(__bf16)u;
+                const float r1 = u - hi;
+                const float mid = (float)(__bf16)r1;
+                bD[g] = as_v16x8(h ? make_uint4(0, 0, 0, 0)
+                                   : make_uint4(pack_bf16x2(hi, mid), pack_bf16x2(r1 - mid, 0.f), 0, 0));
+            }
+            // blocks needing no mask for any of this wave's queries
+            const int full = CAUSAL ? min(qw / BK, N / BK) : N / BK;
+            for (int p = 0; p < it.nblk; ++p, ++gb) {
                 const int k0 = p * BK;
                 if (CAUSAL && k0 >= qw + 64)
-                    zero_step<DH>(smem, p & 1, r4, l);
+                    zero_step<DH>(smem, gb & 1, r4, l);
                 else if (p < full)
-                    score_step<E, DH, false, CAUSAL>(smem, p % NKB, p % NVB, p & 1, k0, qa, N, sc,
+                    score_step<E, DH, false, CAUSAL>(smem, gb % NKB, gb % NVB, gb & 1, k0, qa, N, sc,
                                                      Lq, Dq, qt, gt, so, bD, ones, r4, l);
                 else
-                    score_step<E, DH, true, CAUSAL>(smem, p % NKB, p % NVB, p & 1, k0, qa, N, sc,
+                    score_step<E, DH, true, CAUSAL>(smem, gb % NKB, gb % NVB, gb & 1, k0, qa, N, sc,
                                                     Lq, Dq, qt, gt, so, bD, ones, r4, l);
+                if (p + 1 == it.nblk && more) load_q(Item(run.item(sch, m + 1), nwork, nqb, N));
+                // LDS traffic only: the next item's loads stay in flight
+                __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+                __syncthreads();
             }
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+            if (more) it = Item(run.item(sch, m + 1), nwork, nqb, N);
         }
+        __builtin_amdgcn_s_waitcnt(kLgkmOnly);
+        __syncthreads();  // the gradient waves' last block
+        __builtin_amdgcn_s_waitcnt(0);
         return;
     }
 
@@ -368,8 +424,11 @@ __device__ __forceinline__ void dq_work(
     const int qg0 = DH == 128 ? 4 * (r4 >> 1) : 2 * r4;
     const int dt0 = DH == 128 ? 2 * (r4 & 1) : 0;
     f32x16_t acc[QGW][2];
+    auto zero = [](f32x16_t(&a)[QGW][2]) {
 #pragma unroll
-    for (int i = 0; i < QGW; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+        for (int i = 0; i < QGW; ++i) a[i][0] = a[i][1] = f32x16_t{};
+    };
+    zero(acc);
     using Copier = TileCopier<BK, NWAVE / 2, DH>;
     const Copier cp(r4, l);
     const uint32_t lds0 = lds_addr(smem);
@@ -383,71 +442,87 @@ __device__ __forceinline__ void dq_work(
             ob1[dt] = tile_off<PL::ROWB>(x + 8, colb);
         }
     }
-    for (int p = 0; p <= nblk; ++p) {
-        // copies of block p + 2 first; block p + 1's (issued one phase ago)
-        // must have landed by the barrier, these may stay in flight.  Past
-        // the last block the buffers they fill are read by no one; they are
-        // issued all the same (rows clamped into range), so that no branch
-        // splits the products they are spread over.
-        const int kn = (p + 2) * BK;
-        const uint32_t lk = lds0 + PL::OFF_K + ((p + 2) % NKB) * PL::TILE;
-        const uint32_t lv = lds0 + PL::OFF_V + ((p + 2) % NVB) * PL::TILE;
+    // acc[qg][dt] holds dQ for queries q0 + 32 (qg0 + qg) + 8 (r / 4) + 4 h +
+    // r % 4, column 32 (dt0 + dt) + n
+    auto epilogue = [&](const Item& it) {
+        const long long hoff = it.hoff(N);
+        if constexpr (DIRECT) {
+            e16_t* out = reinterpret_cast<e16_t*>(dq_out) + hoff;
+#pragma unroll
+            for (int qg = 0; qg < QGW; ++qg)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qq = it.q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
+                    e16_t* orow = out + (long long)qq * DH + 32 * dt0 + n;
+                    if (qq < N)
+#pragma unroll
+                        for (int dt = 0; dt < 2; ++dt) {
+                            // the fp32 product first, as the convert step
+                            // forms it (not fused into one mixed-precision
+                            // rounding)
+                            float x = acc[qg][dt][r] * scale;
+                            pin(x);
+                            orow[32 * dt] = (e16_t)(E::pack2(x, 0.f) & 0xffffu);
+                        }
+                }
+        } else {
+            float* out = reinterpret_cast<float*>(dq_out) + hoff;
+#pragma unroll
+            for (int qg = 0; qg < QGW; ++qg)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qq = it.q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
+                    float* orow = out + (long long)qq * DH + 32 * dt0 + n;
+                    if (qq < N)
+#pragma unroll
+                        for (int dt = 0; dt < 2; ++dt) orow[32 * dt] = acc[qg][dt][r];
+                }
+        }
+    };
+    Cursor grd{run.m0, 0, first};  // the next block to reduce
+    Item acc_it = first;           // the item the accumulators belong to
+    for (int g = 0;; ++g) {
+        // copies of block g + 2, spread over the gradient steps; past the
+        // run's last block they are issued all the same (rows clamped into
+        // the last item's head) into buffers no one reads, so that no branch
+        // splits the products they are spread over
+        stg.advance(sch, run, nwork, nqb, N);
+        const long long shoff = stg.it.hoff(N);
+        const int kn = stg.valid(run) ? stg.p * BK : N;
+        const uint32_t lk = lds0 + PL::OFF_K + ((g + 2) % NKB) * PL::TILE;
+        const uint32_t lv = lds0 + PL::OFF_V + ((g + 2) % NVB) * PL::TILE;
         // step t issues slice t (d = 128: two slices per block, d = 64: one)
         auto stage = [&](int j) {
             if (j < Copier::SLICES) {
-                cp.copy(j, Kh, kn, N, lk);
-                cp.copy(j, Vh, kn, N, lv);
+                cp.copy(j, K + shoff, kn, N, lk);
+                cp.copy(j, V + shoff, kn, N, lv);
             }
         };
         static_assert(Copier::SLICES >= 1 && Copier::SLICES <= 2, "at most one slice per 16-key step");
-        if (p >= 1) {
-            grad_step<E, DH>(smem, (p - 1) % NKB, (p - 1) & 1, acc, ob0, ob1, qg0, l, stage);
+        if (g >= 1) {
+            if (grd.p == 0 && grd.m > run.m0) {
+                // the block starts a new item: the previous item's sums are
+                // complete; store them, then start from zero
+                epilogue(acc_it);
+                zero(acc);
+            }
+            if (grd.p == 0) acc_it = grd.it;
+            grad_step<E, DH>(smem, (g - 1) % NKB, (g - 1) & 1, acc, ob0, ob1, qg0, l, stage);
+            grd.advance(sch, run, nwork, nqb, N);
         } else {
 #pragma unroll
             for (int j = 0; j < 2; ++j) stage(j);
         }
-        // block p + 1's copies (issued one phase ago) must have landed; this
-        // phase's 2 SLICES may stay in flight
-        if (p < nblk)
+        // block g + 1's copies (issued one phase ago) must have landed; this
+        // phase's 2 SLICES may stay in flight, except in the last phase
+        if (grd.valid(run))
             __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(2 * Copier::SLICES));
         else
             __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if (!grd.valid(run)) break;
     }
-
-    // epilogue: acc[qg][dt] holds dQ for queries q0 + 32 (qg0 + qg) + 8 (r / 4) +
-    // 4 h + r % 4, column 32 (dt0 + dt) + n
-    if constexpr (DIRECT) {
-        e16_t* out = reinterpret_cast<e16_t*>(dq_out) + hoff;
-#pragma unroll
-        for (int qg = 0; qg < QGW; ++qg)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qq = q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
-                e16_t* orow = out + (long long)qq * DH + 32 * dt0 + n;
-                if (qq < N)
-#pragma unroll
-                    for (int dt = 0; dt < 2; ++dt) {
-                        // the fp32 product first, as the convert step forms
-                        // it (not fused into one mixed-precision rounding)
-                        float x = acc[qg][dt][r] * scale;
-                        pin(x);
-                        orow[32 * dt] = (e16_t)(E::pack2(x, 0.f) & 0xffffu);
-                    }
-            }
-    } else {
-        float* out = reinterpret_cast<float*>(dq_out) + hoff;
-#pragma unroll
-        for (int qg = 0; qg < QGW; ++qg)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qq = q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
-                float* orow = out + (long long)qq * DH + 32 * dt0 + n;
-                if (qq < N)
-#pragma unroll
-                    for (int dt = 0; dt < 2; ++dt) orow[32 * dt] = acc[qg][dt][r];
-            }
-    }
+    epilogue(acc_it);
 }
 
 }  // namespace dqp

@@ -7,6 +7,15 @@
 
 namespace fa {
 
+// Resident workgroups per CU of kernel k launched with `threads` threads (the
+// occupancy query; 1 where the query fails).
+int resident_per_cu(const void* k, int threads);
+
+// Workgroups of a persistent grid over `items` work items: as many as the
+// current device holds at once (its CU count times per_cu), at most `items`;
+// 0 where the device cannot be queried.
+int persistent_grid(long long items, int per_cu);
+
 hipError_t launch_preprocess(int dtype, const void* O, const void* dO, float* D, Shape s,
                              hipStream_t st);
 

@@ -158,13 +158,20 @@ __device__ __forceinline__ void stage_rows(unsigned char* lds_tile, const e16_t*
     }
 }
 
-// The same copy with a scalar base address and a 32-bit per-lane offset.
+// The same copy with a scalar base address and a 32-bit per-lane offset.  base
+// and lds must be the same in every lane; they are read from the first active
+// lane, which states that to the compiler where it cannot prove it (a value
+// carried through a loop of one wave role).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void lds_copy16_sbase(const void* base, uint32_t voff, uint32_t lds) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t ul = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(base), "s"(lds)
+                 : "v"(voff), "s"(reinterpret_cast<const void*>(ua)), "s"(ul)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -242,6 +249,58 @@ __device__ __forceinline__ uint4 pack8(const float* v) {
 __device__ __forceinline__ int xcd_work_item(int bid, int nwork) {
     return (nwork % 8 == 0) ? (bid % 8) * (nwork / 8) + bid / 8 : bid;
 }
+
+// Static schedule of a persistent grid: G workgroups (at most one per CU at a
+// time) run n0 work items of one kind and then n1 of another (n1 = 0: one
+// kind), each workgroup a fixed list of them, so that one item's start can
+// overlap the previous item's end and no workgroup launch sits between them.
+// When n0, n1 and G all divide by 8, XCD x (workgroup b runs on XCD b % 8)
+// takes the x-th eighth of each kind, its share: n0 / 8 positions of kind 0
+// followed by n1 / 8 of kind 1, and the share's P = G / 8 workgroups take its
+// positions in snake order -- round m gives slot s = b / 8 position m P + s
+// for even m, m P + P - 1 - s for odd m -- so that with items sorted heaviest
+// first every workgroup gets about the same work.  Otherwise all items form
+// one share over all G workgroups.  Positions grow with the round, so each
+// workgroup runs its kind-0 items before its kind-1 items.
+struct Schedule {
+    int slot, slots;     // this workgroup's slot in its share, workgroups per share
+    int share0, share1;  // positions of each kind in a share
+    int base0, base1;    // first work item of each kind in this workgroup's share
+
+    __device__ __forceinline__ Schedule(int n0, int n1, int G, int b) {
+        const bool xcd = n0 % 8 == 0 && n1 % 8 == 0 && G % 8 == 0;
+        const int parts = xcd ? 8 : 1, x = xcd ? b % 8 : 0;
+        slot = xcd ? b / 8 : b;
+        slots = G / parts;
+        share0 = n0 / parts;
+        share1 = n1 / parts;
+        base0 = x * share0;
+        base1 = x * share1;
+    }
+    __device__ __forceinline__ int pos(int m) const {
+        return m * slots + ((m & 1) ? slots - 1 - slot : slot);
+    }
+    // first round whose position is at least v
+    __device__ __forceinline__ int first_round(int v) const {
+        const int m = v / slots;
+        return pos(m) < v ? m + 1 : m;
+    }
+};
+
+// The rounds [m0, m1) of one kind in a workgroup's list; round m is work item
+// base + pos(m) - lo of that kind.
+struct Run {
+    int m0, m1, base, lo;
+    __device__ __forceinline__ Run(const Schedule& s, int kind) {
+        lo = kind ? s.share0 : 0;
+        m0 = s.first_round(lo);
+        m1 = s.first_round(kind ? s.share0 + s.share1 : s.share0);
+        base = kind ? s.base1 : s.base0;
+    }
+    __device__ __forceinline__ int item(const Schedule& s, int m) const {
+        return base + s.pos(m) - lo;
+    }
+};
 
 // Causal work item -> (head, rank of its block by work, 0 the heaviest), the
 // heaviest blocks first.  When each XCD's contiguous share of work items
