@@ -27,7 +27,9 @@ hipError_t launch_dq_k(const void* Q, const void* K, const void* V, const void* 
                        int nwork, hipStream_t st) {
     static const int per_cu = resident_per_cu(
         reinterpret_cast<const void*>(&bwd_dq_kernel<E, DH, CAUSAL, DIRECT>), NWAVE * 64);
-    const int G = persistent_grid(nwork, per_cu);
+    // DIRECT: one workgroup per work item (its epilogue cannot sit in the
+    // item loop)
+    const int G = DIRECT ? nwork : persistent_grid(nwork, per_cu);
     if (G <= 0) return hipErrorInvalidDevice;
     hipLaunchKernelGGL((bwd_dq_kernel<E, DH, CAUSAL, DIRECT>), dim3(G), dim3(NWAVE * 64), 0, st,
                        (const e16_t*)Q, (const e16_t*)K, (const e16_t*)V, (const e16_t*)dO, L, Dv,

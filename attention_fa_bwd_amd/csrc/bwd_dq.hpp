@@ -303,7 +303,8 @@ struct QueryCursor {
 // before the first products of the next item.
 // DIRECT: instead of the unscaled fp32 dq_accum, write dQ = scale * acc in the
 // element type (round to nearest even), exactly what the convert step makes of
-// dq_accum; out is then the dQ tensor.
+// dq_accum; out is then the dQ tensor.  A DIRECT run holds one work item (the
+// launcher gives it one workgroup per item).
 template <typename E, int DH, bool CAUSAL, bool DIRECT>
 __device__ __forceinline__ void dq_run(
     const e16_t* __restrict__ Q, const e16_t* __restrict__ K, const e16_t* __restrict__ V,
@@ -500,7 +501,9 @@ __device__ __forceinline__ void dq_run(
         };
         static_assert(Copier::SLICES >= 1 && Copier::SLICES <= 2, "at most one slice per 16-key step");
         if (g >= 1) {
-            if (grd.p == 0 && grd.m > run.m0) {
+            // DIRECT runs one item per workgroup: its 16-bit epilogue inside
+            // the loop would not fit the registers
+            if (!DIRECT && grd.p == 0 && grd.m > run.m0) {
                 // the block starts a new item: the previous item's sums are
                 // complete; store them, then start from zero
                 epilogue(acc_it);

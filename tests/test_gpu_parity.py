@@ -168,6 +168,43 @@ def test_xcd_order_and_head_pairs(d, causal):
     assert errs["o"] <= gu.TOL["bf16"] and errs["L"] <= 1e-3
 
 
+MANY = [(2, 96), (1, 91)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H", MANY, ids=[f"B{b}H{h}" for b, h in MANY])
+def test_many_items_per_workgroup(B, H, d, causal):
+    """More work items than CUs, so every workgroup of the persistent grids
+    runs several items back to back (the next item's first tiles overlap the
+    previous item's last ones), at a ragged N = 300: B=2 H=96 gives item counts
+    divisible by 8 (dK/dV 576, dQ 384: the XCD shares and snake order are on),
+    B=1 H=91 counts that are not (273, 182: one share over all workgroups).
+    Whole tensors against the oracle; the split passes and the no-allocation
+    entry point bitwise equal to fa_bwd's results on the same shape."""
+    import attention_fa_bwd_amd as fa
+    gu.note(f"case many items per workgroup B={B} H={H} N=300 d={d} causal={causal}")
+    inp = si.draw_custom(B, H, 300, d, "bf16", seed=1500 + H + d)
+    out = gu.run_gpu(inp, causal)
+    errs = gu.compare_full(inp, causal, out)
+    gu.note(f"  errs {errs}")
+    _assert_grads(errs, gu.TOL["bf16"], f"B={B} H={H} d={d}")
+    assert errs["o"] <= gu.TOL["bf16"] and errs["L"] <= 1e-3
+    q, k, v, do, L, D = (out[n] for n in ("q", "k", "v", "do", "L", "D"))
+    dqa = torch.full_like(out["dq_accum"], float("nan"))
+    dk, dv = torch.full_like(q, float("nan")), torch.full_like(q, float("nan"))
+    fa.fa_bwd_dq(q, k, v, do, L, D, dqa, inp.wl.scale, causal)
+    fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, inp.wl.scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dqa, out["dq_accum"])
+    assert torch.equal(dk, out["dk"]) and torch.equal(dv, out["dv"])
+    dq2, dk2, dv2 = (torch.full_like(q, float("nan")) for _ in range(3))
+    fa.fa_bwd_noalloc(q, k, v, out["o"], do, L, dq2, dk2, dv2, inp.wl.scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dq2, out["dq"])
+    assert torch.equal(dk2, out["dk"]) and torch.equal(dv2, out["dv"])
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("q_mult", [4.0, 8.0])
