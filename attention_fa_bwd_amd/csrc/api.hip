@@ -186,14 +186,13 @@ int fa_bwd(int dtype, const void* Q, const void* K, const void* V, const void* d
     if ((rc = device_ready()) != FA_OK) return rc;
     const fa::Shape s{B, H, N, d};
     const hipStream_t st = (hipStream_t)stream;
-    // the two passes: dQ (query-outer) and dK/dV (key-outer); on the matrix
-    // cores in one launch, whose grid holds the work items of both
+    // the two passes, dQ (query-outer) and dK/dV (key-outer), in one launch
+    // whose grid holds the work items of both
     if (matrix_core(dtype, d))
         return hip_status(fa::launch_bwd_fused_mfma(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s,
                                                     scale, causal != 0, st));
-    rc = hip_status(launch_dq(dtype, Q, K, V, dO, L, D, dq_accum, s, scale, causal != 0, st));
-    if (rc != FA_OK) return rc;
-    return hip_status(launch_dkdv(dtype, Q, K, V, dO, L, D, dK, dV, s, scale, causal != 0, st));
+    return hip_status(fa::launch_bwd_fused_simt(dtype, Q, K, V, dO, L, D, dq_accum, dK, dV, s,
+                                                scale, causal != 0, st));
 }
 
 int fa_bwd_dkdv(int dtype, const void* Q, const void* K, const void* V, const void* dO,

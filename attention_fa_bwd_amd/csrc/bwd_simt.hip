@@ -82,11 +82,12 @@ __device__ __forceinline__ void simt_stage(float (&dst)[ROWS][D + 1], const T* s
     }
 }
 
+// dK/dV pass, key block kb of head `head` (batch and head folded)
 template <typename T, int D, int BC, int BR, bool CAUSAL>
-__global__ __launch_bounds__(256) void simt_dkdv_kernel(
+__device__ __forceinline__ void simt_dkdv_block(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-    T* __restrict__ dK, T* __restrict__ dV, int N, float scale) {
+    T* __restrict__ dK, T* __restrict__ dV, int N, float scale, int kb, long long head) {
     using W = SimtSplit<D, BC, BR>;
     constexpr int KV_OUT = BC * D / W::NT;  // dK / dV accumulators per lane
     static_assert(KV_OUT >= 1 && KV_OUT * W::NT == BC * D, "tile too small");
@@ -96,9 +97,8 @@ __global__ __launch_bounds__(256) void simt_dkdv_kernel(
     __shared__ float sP[BR][BC + 1], sdS[BR][BC + 1];
     __shared__ float sL[BR], sD[BR];
 
-    const long long head = (long long)blockIdx.z * gridDim.y + blockIdx.y;
     const long long hoff = head * N * D;
-    const int k0 = blockIdx.x * BC;
+    const int k0 = kb * BC;
     const int tid = threadIdx.x;
 
     simt_stage<T, D, BC>(sK, K + hoff, k0, N);
@@ -149,11 +149,12 @@ __global__ __launch_bounds__(256) void simt_dkdv_kernel(
 // DIRECT: instead of the unscaled fp32 dq_accum, write dQ = scale * acc in the
 // element type (round to nearest even), exactly what the convert step makes of
 // dq_accum; out is then the dQ tensor.
+// dQ pass, query block qb of head `head`
 template <typename T, int D, int BC, int BR, bool CAUSAL, bool DIRECT>
-__global__ __launch_bounds__(256) void simt_dq_kernel(
+__device__ __forceinline__ void simt_dq_block(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
-    void* __restrict__ out, int N, float scale) {
+    void* __restrict__ out, int N, float scale, int qb, long long head) {
     using W = SimtSplit<D, BC, BR>;
     constexpr int DQ_OUT = BR * D / W::NT;  // dQ accumulators per lane
     static_assert(DQ_OUT >= 1 && DQ_OUT * W::NT == BR * D, "tile too small");
@@ -163,9 +164,8 @@ __global__ __launch_bounds__(256) void simt_dq_kernel(
     __shared__ float sdS[BR][BC + 1];
     __shared__ float sL[BR], sD[BR];
 
-    const long long head = (long long)blockIdx.z * gridDim.y + blockIdx.y;
     const long long hoff = head * N * D;
-    const int q0 = blockIdx.x * BR;
+    const int q0 = qb * BR;
     const int tid = threadIdx.x;
 
     simt_stage<T, D, BR>(sQ, Q + hoff, q0, N);
@@ -214,6 +214,43 @@ __global__ __launch_bounds__(256) void simt_dq_kernel(
     }
 }
 
+template <typename T, int D, int BC, int BR, bool CAUSAL>
+__global__ __launch_bounds__(256) void simt_dkdv_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+    T* __restrict__ dK, T* __restrict__ dV, int N, float scale) {
+    simt_dkdv_block<T, D, BC, BR, CAUSAL>(Q, K, V, dO, L, Dv, dK, dV, N, scale, blockIdx.x,
+                                          (long long)blockIdx.z * gridDim.y + blockIdx.y);
+}
+
+template <typename T, int D, int BC, int BR, bool CAUSAL, bool DIRECT>
+__global__ __launch_bounds__(256) void simt_dq_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+    void* __restrict__ out, int N, float scale) {
+    simt_dq_block<T, D, BC, BR, CAUSAL, DIRECT>(Q, K, V, dO, L, Dv, out, N, scale, blockIdx.x,
+                                                (long long)blockIdx.z * gridDim.y + blockIdx.y);
+}
+
+// Both passes in one launch (fa_bwd): workgroups x < nqb run dQ-pass blocks,
+// the others dK/dV-pass blocks; they read the same inputs and write disjoint
+// outputs, so nothing orders them, and the results are bitwise those of the
+// two kernels above.
+template <typename T, int D, int BC, int BR, bool CAUSAL>
+__global__ __launch_bounds__(256) void simt_fused_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const float* __restrict__ L, const float* __restrict__ Dv,
+    float* __restrict__ dq_accum, T* __restrict__ dK, T* __restrict__ dV, int N, int nqb,
+    float scale) {
+    const long long head = (long long)blockIdx.z * gridDim.y + blockIdx.y;
+    if ((int)blockIdx.x < nqb)
+        simt_dq_block<T, D, BC, BR, CAUSAL, false>(Q, K, V, dO, L, Dv, dq_accum, N, scale,
+                                                   blockIdx.x, head);
+    else
+        simt_dkdv_block<T, D, BC, BR, CAUSAL>(Q, K, V, dO, L, Dv, dK, dV, N, scale,
+                                              blockIdx.x - nqb, head);
+}
+
 namespace {
 
 // tiles of 16 (d = 128) or 32 rows keep the static LDS within 64 KiB
@@ -251,6 +288,37 @@ hipError_t dq_t(const void* Q, const void* K, const void* V, const void* dO, con
                            (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, out, s.N,
                            scale);
     return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t fused_t(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                   const float* Dv, float* dqa, void* dK, void* dV, Shape s, float scale,
+                   bool causal, hipStream_t st) {
+    constexpr int BT = simt_tile<D>();
+    const int nb = (s.N + BT - 1) / BT;
+    dim3 grid(2 * nb, s.H, s.B);
+    if (causal)
+        hipLaunchKernelGGL((simt_fused_kernel<T, D, BT, BT, true>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, dqa,
+                           (T*)dK, (T*)dV, s.N, nb, scale);
+    else
+        hipLaunchKernelGGL((simt_fused_kernel<T, D, BT, BT, false>), grid, dim3(256), 0, st,
+                           (const T*)Q, (const T*)K, (const T*)V, (const T*)dO, L, Dv, dqa,
+                           (T*)dK, (T*)dV, s.N, nb, scale);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t fused_d(const void* Q, const void* K, const void* V, const void* dO, const float* L,
+                   const float* Dv, float* dqa, void* dK, void* dV, Shape s, float scale,
+                   bool causal, hipStream_t st) {
+    switch (s.d) {
+        case 16: return fused_t<T, 16>(Q, K, V, dO, L, Dv, dqa, dK, dV, s, scale, causal, st);
+        case 32: return fused_t<T, 32>(Q, K, V, dO, L, Dv, dqa, dK, dV, s, scale, causal, st);
+        case 64: return fused_t<T, 64>(Q, K, V, dO, L, Dv, dqa, dK, dV, s, scale, causal, st);
+        case 128: return fused_t<T, 128>(Q, K, V, dO, L, Dv, dqa, dK, dV, s, scale, causal, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename T>
@@ -295,6 +363,15 @@ hipError_t launch_bwd_dkdv_simt(int dtype, const void* Q, const void* K, const v
     return dtype == DT_BF16   ? dkdv_d<bf16_t>(Q, K, V, dO, L, D, dK, dV, s, scale, causal, st)
            : dtype == DT_F16  ? dkdv_d<f16_t>(Q, K, V, dO, L, D, dK, dV, s, scale, causal, st)
                               : dkdv_d<float>(Q, K, V, dO, L, D, dK, dV, s, scale, causal, st);
+}
+
+hipError_t launch_bwd_fused_simt(int dtype, const void* Q, const void* K, const void* V,
+                                 const void* dO, const float* L, const float* D, float* dq_accum,
+                                 void* dK, void* dV, Shape s, float scale, bool causal,
+                                 hipStream_t st) {
+    return dtype == DT_BF16  ? fused_d<bf16_t>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st)
+           : dtype == DT_F16 ? fused_d<f16_t>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st)
+                             : fused_d<float>(Q, K, V, dO, L, D, dq_accum, dK, dV, s, scale, causal, st);
 }
 
 hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const void* V,

@@ -43,6 +43,11 @@ hipError_t launch_bwd_dkdv_simt(int dtype, const void* Q, const void* K, const v
 hipError_t launch_bwd_dq_simt(int dtype, const void* Q, const void* K, const void* V,
                               const void* dO, const float* L, const float* D, float* dq_accum,
                               Shape s, float scale, bool causal, hipStream_t st);
+// Both vector-ALU passes in one launch (fa_bwd).
+hipError_t launch_bwd_fused_simt(int dtype, const void* Q, const void* K, const void* V,
+                                 const void* dO, const float* L, const float* D, float* dq_accum,
+                                 void* dK, void* dV, Shape s, float scale, bool causal,
+                                 hipStream_t st);
 // The same dQ pass writing dQ = scale * dq_accum in the element type directly.
 hipError_t launch_bwd_dq_simt_direct(int dtype, const void* Q, const void* K, const void* V,
                                      const void* dO, const float* L, const float* D, void* dQ,
