@@ -42,6 +42,8 @@
 //     stored.
 #pragma once
 
+#include <type_traits>
+
 #include "mfma_common.hpp"
 
 namespace fa {
@@ -441,12 +443,13 @@ __device__ __forceinline__ void dkdv_run(
     // d 32 (db0 + db) + 8 (r / 4) + 4 h + r % 4
     e16_t* const out = is_dk ? dK : dV;
     const float osc = is_dk ? scale : 1.f;
-    auto epilogue = [&](const Item& it) {
+    auto store_rows = [&](const Item& it, auto ragged_tag) {
+        constexpr bool RAGGED = decltype(ragged_tag)::value;
         const long long hoff = it.hoff(N);
 #pragma unroll
         for (int kg = 0; kg < KG; ++kg) {
             const int kk = it.k0 + 32 * (kg0 + kg) + n;
-            if (kk >= N) continue;
+            if (RAGGED && kk >= N) continue;
             e16_t* row = out + hoff + (long long)kk * DH;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
@@ -460,6 +463,14 @@ __device__ __forceinline__ void dkdv_run(
                     *reinterpret_cast<uint2*>(row + d0) = v;
                 }
         }
+    };
+    // a block wholly inside N (every block but a ragged last one) stores
+    // without a per-row test
+    auto epilogue = [&](const Item& it) {
+        if (it.k0 + BC <= N)
+            store_rows(it, std::false_type{});
+        else
+            store_rows(it, std::true_type{});
     };
     KeyCursor<DH, CAUSAL> stg{run.m0, 0, first};  // the tile staged last
     KeyCursor<DH, CAUSAL> grd{run.m0, 0, first};  // the next tile to reduce

@@ -40,6 +40,8 @@
 //     stored.
 #pragma once
 
+#include <type_traits>
+
 #include "mfma_common.hpp"
 
 namespace fa {
@@ -445,7 +447,10 @@ __device__ __forceinline__ void dq_run(
     }
     // acc[qg][dt] holds dQ for queries q0 + 32 (qg0 + qg) + 8 (r / 4) + 4 h +
     // r % 4, column 32 (dt0 + dt) + n
-    auto epilogue = [&](const Item& it) {
+    // a block wholly inside N (every block but a ragged last one) stores
+    // without a per-row test
+    auto store_rows = [&](const Item& it, auto ragged_tag) {
+        constexpr bool RAGGED = decltype(ragged_tag)::value;
         const long long hoff = it.hoff(N);
         if constexpr (DIRECT) {
             e16_t* out = reinterpret_cast<e16_t*>(dq_out) + hoff;
@@ -455,7 +460,7 @@ __device__ __forceinline__ void dq_run(
                 for (int r = 0; r < 16; ++r) {
                     const int qq = it.q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
                     e16_t* orow = out + (long long)qq * DH + 32 * dt0 + n;
-                    if (qq < N)
+                    if (!RAGGED || qq < N)
 #pragma unroll
                         for (int dt = 0; dt < 2; ++dt) {
                             // the fp32 product first, as the convert step
@@ -474,11 +479,17 @@ __device__ __forceinline__ void dq_run(
                 for (int r = 0; r < 16; ++r) {
                     const int qq = it.q0 + 32 * (qg0 + qg) + 8 * (r >> 2) + 4 * h + (r & 3);
                     float* orow = out + (long long)qq * DH + 32 * dt0 + n;
-                    if (qq < N)
+                    if (!RAGGED || qq < N)
 #pragma unroll
                         for (int dt = 0; dt < 2; ++dt) orow[32 * dt] = acc[qg][dt][r];
                 }
         }
+    };
+    auto epilogue = [&](const Item& it) {
+        if (it.q0 + BQ <= N)
+            store_rows(it, std::false_type{});
+        else
+            store_rows(it, std::true_type{});
     };
     Cursor grd{run.m0, 0, first};  // the next block to reduce
     Item acc_it = first;           // the item the accumulators belong to
