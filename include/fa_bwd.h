@@ -35,12 +35,17 @@
  *              and d (the library cannot check this: a smaller buffer is read
  *              or written out of bounds).  Outputs must not alias inputs.
  *              The library allocates nothing; its only mutable global state
- *              is fa_bwd_noalloc's static scratch array (see there).  Calls
- *              on different streams may run concurrently as long as their
+ *              is fa_bwd_noalloc's static scratch array (see there) and
+ *              device properties it queries once and keeps (each device's CU
+ *              count, the kernels' resident workgroups per CU).  Calls on
+ *              different streams may run concurrently as long as their
  *              buffers are disjoint (fa_bwd_noalloc calls excepted).
  *   Stream     `stream` is a hipStream_t passed as void*; NULL is the null
  *              stream.  Every call only enqueues work and returns; the caller
- *              synchronises.
+ *              synchronises.  No call allocates, clears memory with a memset
+ *              or synchronises, so calls can be captured into a HIP graph
+ *              (after one eager call on the device, which makes the one-time
+ *              queries).
  *   Sizes      B, H, N, d >= 1; B * H * N * d < 2^40; B and H < 65536.
  *              Supported head dims: d in {16, 32, 64, 128} for every dtype.
  *   Errors     every call returns an fa_status_t.  Arguments are validated
@@ -122,8 +127,9 @@ int fa_bwd_preprocess(int dtype, const void* O, const void* dO, float* D,
  * dP = dO V^T and dS = P (dP - D), and accumulates dV = P^T dO and dK = dS^T Q
  * per key block (dK multiplied by `scale` at write-out, sec 16.6) and
  * dQ = dS K (unscaled) per query block; under the causal mask, tiles wholly
- * above the diagonal are skipped (sec 16.8 item 2).  It is fa_bwd_dq followed
- * by fa_bwd_dkdv on the same stream.
+ * above the diagonal are skipped (sec 16.8 item 2).  It runs both passes in
+ * one launch, and its results are bitwise those of fa_bwd_dq followed by
+ * fa_bwd_dkdv on the same stream.
  *   One contract for every dtype and head dim: dq_accum is overwritten (its
  *   prior contents are never read), no atomics are used, and dq_accum, dK
  *   and dV are bitwise reproducible from call to call.  bf16 and fp16 with
