@@ -124,11 +124,14 @@ def calibrate_copy():
                       "launches": 5}))
 
 
-# Algorithmic FLOPs per (b, h), as a multiple of N^2 d before the causal
-# halving: the dK/dV pass recomputes S and dP and forms dV and dK (4 of the 5
-# products), the dQ pass recomputes S and dP and forms dQ (3 products);
-# fa_bwd runs both (one launch on the matrix cores).
-KERNEL_FLOP_FACTOR = {"fa_bwd": 14.0, "fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
+# FLOPs per (b, h) as a multiple of N^2 d, before the causal halving.
+# Algorithmic (the method's five products, FA2 chapter 16 sec 16.7: S, dP, dV,
+# dK, dQ, 2 N^2 d each): fa_bwd does all five; of its two passes, the dK/dV
+# pass forms S, dP, dV and dK (8) and the dQ pass forms dQ (2) -- its own S
+# and dP are recomputation.  Executed (the products the kernels issue): the dQ
+# pass forms S and dP again, 6 instead of 2, so fa_bwd issues 14.
+KERNEL_FLOP_FACTOR = {"fa_bwd": 10.0, "fa_bwd_dkdv": 8.0, "fa_bwd_dq": 2.0}
+EXECUTED_FLOP_FACTOR = {"fa_bwd": 14.0, "fa_bwd_dkdv": 8.0, "fa_bwd_dq": 6.0}
 
 
 def elem_bytes(wl) -> int:
@@ -142,9 +145,21 @@ def hbm_kernel_bytes(wl) -> dict:
             "fa_bwd_convert_dq": rows * wl.d * (4 + es)}            # read dq_accum; write dQ
 
 
-def pass_flops(wl, causal: bool, kernel: str) -> float:
-    f = KERNEL_FLOP_FACTOR[kernel] * wl.B * wl.H * wl.N * wl.N * wl.d
+def pass_flops(wl, causal: bool, kernel: str, executed: bool = False) -> float:
+    factor = (EXECUTED_FLOP_FACTOR if executed else KERNEL_FLOP_FACTOR)[kernel]
+    f = factor * wl.B * wl.H * wl.N * wl.N * wl.d
     return 0.5 * f if causal else f
+
+
+def kernel_rates(wl, causal: bool, kernel: str, ms: float, peak: float) -> dict:
+    """A kernel's rate on its algorithmic FLOPs (the roofline figures) and on
+    the FLOPs it executes (how busy the unit is)."""
+    kf, ke = pass_flops(wl, causal, kernel), pass_flops(wl, causal, kernel, executed=True)
+    return {"avg_launch_ms": round(ms, 5), "flop_per_launch": kf,
+            "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
+            "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4),
+            "executed_flop_per_launch": ke,
+            "executed_frac": round(ke / (ms * 1e-3) / 1e12 / peak, 4)}
 
 
 def compute_peak(wl):
@@ -238,11 +253,7 @@ def passes_alone(wl, causal: bool, inputs, reps: int = 5) -> dict:
     for name, fn in (("fa_bwd_dq", lambda: fa.fa_bwd_dq(q, k, v, do, L, D, dqa, wl.scale, causal, stream)),
                      ("fa_bwd_dkdv", lambda: fa.fa_bwd_dkdv(q, k, v, do, L, D, dk, dv, wl.scale,
                                                             causal, stream))):
-        ms = timed_reps(fn, reps)
-        kf = pass_flops(wl, causal, name)
-        out[name] = {"avg_launch_ms": round(ms, 5), "flop_per_launch": kf,
-                     "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
-                     "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4)}
+        out[name] = kernel_rates(wl, causal, name, timed_reps(fn, reps), peak)
     return out
 
 
@@ -369,10 +380,7 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
     tflops = flops / (r["ms_per_step"] * 1e-3) / 1e12
     bound, peak = compute_peak(wl)
     kernels = {}
-    kf, ms = pass_flops(wl, causal, "fa_bwd"), r["kernel_ms"]["fa_bwd"]
-    kernels["fa_bwd"] = {"avg_launch_ms": round(ms, 5), "flop_per_launch": kf,
-                         "achieved": round(kf / (ms * 1e-3) / 1e12, 3),
-                         "frac": round(kf / (ms * 1e-3) / 1e12 / peak, 4)}
+    kernels["fa_bwd"] = kernel_rates(wl, causal, "fa_bwd", r["kernel_ms"]["fa_bwd"], peak)
     for kname, nbytes in hbm_kernel_bytes(wl).items():
         ms = r["kernel_ms"][kname]
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -396,7 +404,8 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
                      "unit": "TFLOP/s", "frac": kd["frac"],
                      "traffic": load_traffic(wl.name, causal, dom),
                      "flop_per_launch": kd["flop_per_launch"],
-                     "avg_launch_ms": kd["avg_launch_ms"]},
+                     "avg_launch_ms": kd["avg_launch_ms"],
+                     "executed_frac": kd["executed_frac"]},
         "kernels": kernels,
         "passes_alone": alone,
     }

@@ -55,9 +55,19 @@ def test_flop_and_byte_models():
     wl = si.WORKLOADS["h32_n8192_d128_bf16"]
     f = wl.flops(False)
     assert f == 10 * 32 * 8192 ** 2 * 128 and wl.flops(True) == f / 2
+    # algorithmic: the five products, split 8 : 2 between the passes
+    assert bench.pass_flops(wl, False, "fa_bwd") == f
     assert bench.pass_flops(wl, False, "fa_bwd_dkdv") == 0.8 * f
-    assert bench.pass_flops(wl, True, "fa_bwd") == 0.7 * f
-    assert bench.pass_flops(wl, True, "fa_bwd_dq") == 0.3 * f
+    assert bench.pass_flops(wl, True, "fa_bwd") == 0.5 * f
+    assert bench.pass_flops(wl, True, "fa_bwd_dq") == 0.1 * f
+    assert (bench.pass_flops(wl, False, "fa_bwd_dkdv") + bench.pass_flops(wl, False, "fa_bwd_dq")
+            == bench.pass_flops(wl, False, "fa_bwd"))
+    # executed: the dQ pass forms S and dP again
+    assert bench.pass_flops(wl, False, "fa_bwd", executed=True) == 1.4 * f
+    assert bench.pass_flops(wl, True, "fa_bwd_dq", executed=True) == 0.3 * f
+    r = bench.kernel_rates(wl, False, "fa_bwd", 2.0, bench.PEAK_BF16_TFLOPS)
+    assert r["frac"] == round(f / 2e-3 / 1e12 / bench.PEAK_BF16_TFLOPS, 4)
+    assert abs(r["executed_frac"] - 1.4 * r["frac"]) < 1e-3
     rows = 32 * 8192
     b = bench.hbm_kernel_bytes(wl)
     assert b["fa_bwd_preprocess"] == rows * 128 * 4 + rows * 4
