@@ -110,7 +110,10 @@ def test_edge_shapes(N, d, dtype, causal):
     (2) End to end (GPU forward, then backward) against the plain definition,
         for N >= 16.  Below that, D formed from a bf16-stored O can dominate:
         with two keys dS is a small difference (N=2 emulated on the CPU gives
-        2.2e-2 on dK), so only (1) applies there."""
+        2.2e-2 on dK), so the chain is checked link by link instead: the GPU
+        forward's O and L against the oracle's forward, then the GPU backward
+        that consumed them against the oracle's key-outer backward fed the
+        very same stored O and L."""
     gu.note(f"case edge N={N} d={d} {dtype} causal={causal}")
     inp = si.draw_custom(1, 2, N, d, dtype, seed=100 + N + d)
     scale = inp.wl.scale
@@ -121,10 +124,18 @@ def test_edge_shapes(N, d, dtype, causal):
     errs = {n: gu.rel_err(gu.to_f64(out[n]), r) for n, r in (("dq", rq), ("dk", rk), ("dv", rv))}
     _assert_grads(errs, gu.TOL[dtype], f"isolated N={N} d={d} {dtype}")
     assert not gu.invariants(inp, causal, out)["nan"]
+    out = gu.run_gpu(inp, causal)
     if N >= 16 or dtype == "fp32":
-        out = gu.run_gpu(inp, causal)
         errs = gu.compare_full(inp, causal, out)
         _assert_grads(errs, gu.TOL[dtype], f"N={N} d={d} {dtype}")
+    else:
+        eo = gu.rel_err(gu.to_f64(out["o"]), O)
+        el = float(np.abs(gu.to_f64(out["L"]) - L).max())
+        assert eo <= gu.TOL[dtype] and el <= 1e-4, f"forward N={N}: O {eo:.3e}, L {el:.3e}"
+        Og, Lg = gu.to_f64(out["o"]), gu.to_f64(out["L"])
+        rq, rk, rv = oracle.flash_bwd_tiled(inp.Q, inp.K, inp.V, Og, inp.dO, Lg, scale, causal, 16, 12)
+        errs = {n: gu.rel_err(gu.to_f64(out[n]), r) for n, r in (("dq", rq), ("dk", rk), ("dv", rv))}
+        _assert_grads(errs, gu.TOL[dtype], f"chained N={N} d={d} {dtype}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
