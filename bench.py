@@ -66,6 +66,8 @@ def parse(argv=None):
                    help="oracle time budget for the line's own workload (others: a third of it)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain 512 MiB device copy (HBM counter calibration)")
+    p.add_argument("--reference-gemm", action="store_true",
+                   help="run only the library bf16 GEMM reference (for its counter profile)")
     return p.parse_args(argv)
 
 
@@ -308,6 +310,24 @@ def extras(wl, causal: bool, inputs, step_ms: float, flops: float) -> dict:
     }
 
 
+def matmul_reference(n: int = 16384, reps: int = 5) -> dict:
+    """A plain library bf16 GEMM (torch.matmul, dispatched to hipBLASLt) on the
+    same GPU, timed like the kernels: the matrix-core rate a vendor-tuned dense
+    product sustains on this device under load.  The backward's rate on the
+    products it issues is read against it (a dense GEMM is the best case for
+    the matrix cores: no softmax, no recomputation, no barriers per tile)."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = timed_reps(lambda: torch.matmul(a, b, out=c), reps=reps)
+    del a, b, c
+    torch.cuda.empty_cache()
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"op": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt)", "ms": round(ms, 4),
+            "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_host() -> str:
     model = "unknown CPU"
     try:
@@ -428,6 +448,9 @@ def main(argv=None):
     if args.calibrate_copy:
         calibrate_copy()
         return
+    if args.reference_gemm:
+        print(json.dumps({"matmul_reference": matmul_reference()}), flush=True)
+        return
     runs = plan(args)
     results = []
     for i, (name, causal) in enumerate(runs):
@@ -462,6 +485,13 @@ def main(argv=None):
     for key in ("forward", "recompute_L", "forward_backward"):
         if key in prim:
             line[key] = prim[key]
+    if not args.no_extra:
+        ref = matmul_reference()
+        fb = prim["kernels"]["fa_bwd"]
+        # the backward's products issued per second over the library GEMM's
+        ref["fa_bwd_executed_over_matmul"] = round(
+            fb["executed_flop_per_launch"] / (fb["avg_launch_ms"] * 1e-3) / 1e12 / ref["tflops"], 3)
+        line["matmul_reference"] = ref
     line["cpu_baseline"] = prim["cpu_baseline"]
     line["configs"] = results
     print(json.dumps(line), flush=True)

@@ -23,7 +23,9 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_default_run_times_every_config():
-    runs = bench.plan(bench.parse([]))
+    args = bench.parse([])
+    assert not args.reference_gemm and bench.parse(["--reference-gemm"]).reference_gemm
+    runs = bench.plan(args)
     assert runs[0] == ("h32_n8192_d128_bf16", False)
     assert sorted(runs) == sorted(bench.CONFIGS)
     assert len(set(runs)) == 7
