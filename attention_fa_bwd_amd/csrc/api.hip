@@ -55,6 +55,8 @@ int hip_status(hipError_t e) {
 bool dims_ok(int B, int H, int N, int d) {
     if (B < 1 || H < 1 || N < 1 || d < 1) return false;
     if (B >= 65536 || H >= 65536) return false;
+    // row and tile indices (N plus a few tile sizes) are 32-bit in the kernels
+    if (N > (1 << 30)) return false;
     const long long e = (long long)B * H * N * d;
     return e < (1LL << 40);
 }

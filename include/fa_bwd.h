@@ -46,7 +46,8 @@
  *              or synchronises, so calls can be captured into a HIP graph
  *              (after one eager call on the device, which makes the one-time
  *              queries).
- *   Sizes      B, H, N, d >= 1; B * H * N * d < 2^40; B and H < 65536.
+ *   Sizes      B, H, N, d >= 1; B * H * N * d < 2^40; B and H < 65536;
+ *              N <= 2^30 (row and tile indices are 32-bit).
  *              Supported head dims: d in {16, 32, 64, 128} for every dtype.
  *   Errors     every call returns an fa_status_t.  Arguments are validated
  *              before any device work: FA_EINVAL for a NULL pointer, a

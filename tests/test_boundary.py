@@ -60,6 +60,8 @@ def test_invalid_arguments_rejected_before_device_work():
     assert _bwd(lib, dtype=7) == fa.FA_EINVAL
     assert _bwd(lib, B=70000) == fa.FA_EINVAL
     assert _bwd(lib, B=60000, H=60000, N=60000, d=128) == fa.FA_EINVAL   # > 2^40 elements
+    assert _bwd(lib, N=(1 << 30) + 1, d=16) == fa.FA_EINVAL              # N beyond 32-bit tile indices
+    assert _bwd(lib, N=2**31 - 1, d=16) == fa.FA_EINVAL
     p = ALIGNED
     assert lib.fa_fwd_lse(1, p, p, None, p, p, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
     assert lib.fa_lse(1, p, p, None, 1, 1, 8, 64, 0.1, 0, None) == fa.FA_EINVAL
