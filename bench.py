@@ -212,19 +212,26 @@ def gpu_time(wl, causal: bool, steps: int, warmup: int, inputs):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: K whole steps; HIP events on the launch stream split it per kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    # timed region: K whole steps and nothing else on the stream, between two
+    # HIP events (an event recorded between the calls costs a few microseconds,
+    # which would weigh on the small workloads' steps)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(steps):
-        step(evs[i])
+    for _ in range(steps):
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
+    # the same K steps once more with HIP events on the launch stream between
+    # the calls: each call's duration, and each step's
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     split = {name: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, name in enumerate(STEP_CALLS)}
     per_step = [e[0].elapsed_time(e[3]) for e in evs]
     return {
@@ -390,12 +397,18 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
     del inp
     o, L = fa.forward(q, k, v, wl.scale, causal)
     torch.cuda.synchronize()
-    steps = args.steps
+    steps, warmup = args.steps, args.warmup
     if not primary:
+        # short steps: time at least ~100 ms after ~50 ms of warm-up, so that
+        # the device has left its idle clocks (the oracle's CPU baseline of the
+        # previous entry leaves it idle for seconds) and one host-side delay
+        # does not dominate the mean
         probe = gpu_time(wl, causal, 3, 1, (q, k, v, do, o, L))
-        if probe["step_ms"]["median"] < 1.0:
-            steps = max(steps, 200)
-    r = gpu_time(wl, causal, steps, args.warmup, (q, k, v, do, o, L))
+        per = probe["step_ms"]["median"]
+        if per < 1.0:
+            steps = max(steps, 200, int(100.0 / per))
+            warmup = max(warmup, int(50.0 / per))
+    r = gpu_time(wl, causal, steps, warmup, (q, k, v, do, o, L))
     flops = wl.flops(causal)
     tflops = flops / (r["ms_per_step"] * 1e-3) / 1e12
     bound, peak = compute_peak(wl)
@@ -414,12 +427,13 @@ def bench_config(name: str, causal: bool, args, with_extras: bool, cpu_budget: f
                     f"{' Q x %g' % wl.q_mult if wl.q_mult != 1.0 else ''} "
                     f"{'causal' if causal else 'non-causal'}",
         "name": wl.name, "causal": causal, "dtype": wl.dtype,
-        "flop_per_step": flops, "steps": steps,
+        "flop_per_step": flops, "steps": steps, "warmup": warmup,
         "value": round(tflops, 4), "unit": "TFLOP/s",
         "ms_per_step": round(r["ms_per_step"], 5),
         "pct_bf16_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 3),
         "step_ms": r["step_ms"],
         "split_ms": {kk: round(vv, 5) for kk, vv in r["kernel_ms"].items()},
+        "split_method": "a second pass of the same steps with HIP events between the calls",
         "roofline": {"bound": bound, "kernel": dom, "achieved": kd["achieved"], "peak": peak,
                      "unit": "TFLOP/s", "frac": kd["frac"],
                      "traffic": load_traffic(wl.name, causal, dom),
