@@ -233,8 +233,7 @@ __device__ __forceinline__ void score_step(unsigned char* smem, int qbuf, int pb
 // slabs (one per key group, each feeding two), read two steps ahead.
 // ob0 / ob1: the lane's transposing-read offsets of rows 4 h + (l % 16) / 4
 // and that + 8 in each d block (rows 16 t + ... share their swizzle).
-// FIRST: the tile is its work item's first; the accumulators start from zero.
-template <typename E, int DH, bool FIRST>
+template <typename E, int DH>
 __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, int pbuf, bool dk,
                                           f32x16_t (&acc)[2][DH / 32], const int (&ob0)[2],
                                           const int (&ob1)[2], int kg0, int l) {
@@ -264,8 +263,7 @@ __device__ __forceinline__ void grad_step(const unsigned char* smem, int qbuf, i
         for (int kg = 0; kg < KG; ++kg)
 #pragma unroll
             for (int db = 0; db < 2; ++db)
-                acc[db][kg] = E::mma(a[t % 3][db], b[t % 3][kg],
-                                     FIRST && t == 0 ? f32x16_t{} : acc[db][kg]);
+                acc[db][kg] = E::mma(a[t % 3][db], b[t % 3][kg], acc[db][kg]);
         __builtin_amdgcn_sched_barrier(0);
     }
 }
@@ -499,7 +497,7 @@ __device__ __forceinline__ void dkdv_run(
                 zero(acc);
             }
             if (grd.p == 0) acc_it = grd.it;
-            grad_step<E, DH, false>(smem, qbp, pb ^ 1, is_dk, acc, ob0, ob1, kg0, l);
+            grad_step<E, DH>(smem, qbp, pb ^ 1, is_dk, acc, ob0, ob1, kg0, l);
             grd.advance(sch, run, nwork, nkb, N);
         }
         __builtin_amdgcn_s_waitcnt(0);

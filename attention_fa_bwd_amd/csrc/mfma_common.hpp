@@ -235,15 +235,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
         (int)(uintptr_t)FA_LDS(const unsigned char, p));
 }
 
-__device__ __forceinline__ uint4 pack8(const float* v) {
-    uint4 u;
-    u.x = pack_bf16x2(v[0], v[1]);
-    u.y = pack_bf16x2(v[2], v[3]);
-    u.z = pack_bf16x2(v[4], v[5]);
-    u.w = pack_bf16x2(v[6], v[7]);
-    return u;
-}
-
 // Workgroup id -> work item so that consecutive work items share an XCD
 // (workgroups are dealt to the 8 XCDs round-robin by id).
 __device__ __forceinline__ int xcd_work_item(int bid, int nwork) {
